@@ -1,0 +1,172 @@
+"""ctypes binding of the C-ABI library declared in include/exact_attn.h.
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory (the tensors) and the current HIP stream.  There is no CPU
+fallback: if the library is missing, or a tensor is not on the GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "library_path", "load_library",
+           "STATUS", "EXPORTED_SYMBOLS"]
+
+LIB_NAME = "libexact_attn.so"
+
+DTYPE_CODES = {torch.float16: 0, torch.bfloat16: 1}
+
+STATUS = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_INVALID_ARG",
+    2: "ATTN_ERR_UNSUPPORTED_HEAD_DIM",
+    3: "ATTN_ERR_UNSUPPORTED_DTYPE",
+    4: "ATTN_ERR_MISALIGNED",
+    5: "ATTN_ERR_TOO_LARGE",
+    6: "ATTN_ERR_HIP",
+}
+
+# (name, restype, argtypes) for every function include/exact_attn.h declares
+_P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+EXPORTED_SYMBOLS = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                             _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_hip_error": (_I, []),
+}
+
+_LIB = None
+_LOCK = threading.Lock()
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library (or a tensor it cannot take)."""
+
+    def __init__(self, msg: str, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+
+def load_library():
+    """Load the built HIP library once and declare its signatures."""
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise AttnError(f"HIP library {path} is not built; run __graft_entry__.build()")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in EXPORTED_SYMBOLS.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _LIB = lib
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.attn_status_string(status).decode()
+        if status == 6:
+            msg += f" (hipError_t {lib.attn_last_hip_error()})"
+        raise AttnError(f"{what}: {msg}", status)
+
+
+def _device_tensor(x: torch.Tensor, name: str) -> None:
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise AttnError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if not x.is_contiguous():
+        raise AttnError(f"{name} must be contiguous")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             window_left: int = -1, window_right: int = -1,
+             softmax_scale: float | None = None, out: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Dense attention forward.  q, k, v: [B, H, N, d] fp16/bf16 on one GPU.
+
+    Returns (o, lse) with o like q and lse fp32 [B, H, N] (lse is None if return_lse is False
+    and no lse buffer was given).  Launches on the current stream."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise AttnError("q, k, v must all be [B, H, N, d] with equal shapes")
+    if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise AttnError("q, k, v must share one dtype: float16 or bfloat16")
+    bsz, nh, n, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _device_tensor(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise AttnError("out must match q in shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, nh, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _device_tensor(lse, "lse")
+        if lse.shape != (bsz, nh, n) or lse.dtype != torch.float32:
+            raise AttnError("lse must be float32 [B, H, N]")
+    lib = load_library()
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
+                      DTYPE_CODES[q.dtype], float(softmax_scale), int(bool(causal)),
+                      int(window_left), int(window_right), _stream_handle(q.device))
+    _check(st, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                    window_left: int = -1, window_right: int = -1,
+                    softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Packed variable-length forward.  q, k, v: [H, total, d]; cu_seqlens: int32 GPU tensor
+    [num_seqs + 1]; max_seqlen: a host bound on the sequence lengths.
+    Returns (o [H, total, d], lse fp32 [H, total])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens")):
+        _device_tensor(t, n)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise AttnError("q, k, v must all be [H, total_tokens, d] with equal shapes")
+    if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise AttnError("q, k, v must share one dtype: float16 or bfloat16")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise AttnError("cu_seqlens must be a 1-D int32 tensor of num_seqs + 1 entries")
+    nh, total, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _device_tensor(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise AttnError("out must match q in shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((nh, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _device_tensor(lse, "lse")
+        if lse.shape != (nh, total) or lse.dtype != torch.float32:
+            raise AttnError("lse must be float32 [H, total_tokens]")
+    lib = load_library()
+    st = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen),
+                             total, nh, d, DTYPE_CODES[q.dtype], float(softmax_scale),
+                             int(bool(causal)), int(window_left), int(window_right),
+                             _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen")
+    return out, lse

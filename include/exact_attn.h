@@ -1,0 +1,102 @@
+/*
+ * exact_attn.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The library computes the FlashAttention-2 forward pass (page "flash_attn_mma_tiling_qk.cu",
+ * header comment and kernel: each block takes a tile of Q rows, streams every K/V tile of the
+ * sequence, keeps a running row max and row sum, rescales the O accumulator and normalises O at
+ * the end).  The result is the plain softmax(scale * Q K^T + mask) V, plus the per-row
+ * log-sum-exp of the scaled, masked scores.
+ *
+ * Conventions shared by both entry points
+ *   - q, k, v, o hold fp16 or bf16 values, contiguous, head_dim fastest.  They are DEVICE
+ *     pointers owned by the caller and must be 16-byte aligned.  o must not alias q, k or v.
+ *   - lse, if not NULL, is a DEVICE fp32 array owned by the caller (4-byte aligned).  It
+ *     receives the NATURAL-log log-sum-exp of each row; a row that sees no key gets -inf and
+ *     O = 0 (page "flash_fwd_kernel.h" @26a6e0a, consumer loop: empty tiles store zeros).
+ *   - softmax_scale multiplies Q K^T; it must be finite and > 0 (usually 1/sqrt(head_dim)).
+ *   - Masks (page "mainloop_bwd_sm90_tma_gmma_ws.hpp", `mma`: causal masking iterations and the
+ *     Is_local branch; here seqlen_q == seqlen_k): key j is visible to query i iff
+ *         (causal == 0 || j <= i)
+ *      && (window_left  < 0 || j >= i - window_left)
+ *      && (window_right < 0 || j <= i + window_right).
+ *     causal must be 0 or 1; window_left/window_right are >= 0, or -1 for unbounded.
+ *     causal = 1 is the window mask with window_right = 0.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls are asynchronous: they only
+ *     enqueue kernels.  The library allocates no memory and keeps no state except a cached
+ *     device query, so concurrent calls from several threads are safe.
+ *   - Errors are returned, never thrown or printed; nothing is launched when the arguments
+ *     fail validation.  Arguments are validated on the host only: the contents of device
+ *     arrays (cu_seqlens) are trusted.
+ *   - Supported head_dim: 64, 128, 256, 512.  Supported dtype: ATTN_DTYPE_FP16,
+ *     ATTN_DTYPE_BF16.  Any sequence length is accepted (no tile-multiple requirement).
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+enum {
+  ATTN_DTYPE_FP16 = 0,
+  ATTN_DTYPE_BF16 = 1
+};
+
+/* Status codes returned by every entry point. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,          /* null pointer, bad size, scale or mask argument      */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 2, /* head_dim not in {64, 128, 256, 512}                 */
+  ATTN_ERR_UNSUPPORTED_DTYPE = 3,    /* dtype not fp16 / bf16                               */
+  ATTN_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte or lse/cu_seqlens not 4-byte    */
+  ATTN_ERR_TOO_LARGE = 5,            /* a size would overflow the kernel's index arithmetic */
+  ATTN_ERR_HIP = 6                   /* the HIP runtime reported an error at launch         */
+};
+
+/*
+ * attn_fwd - dense batch.
+ *   q, k, v, o : [batch, heads, seqlen, head_dim]
+ *   lse        : [batch, heads, seqlen] fp32, or NULL
+ * batch, heads, seqlen >= 0 (a zero size is a no-op that returns ATTN_OK).
+ * Defined by page "flash_attn_mma_tiling_qk.cu" (problem statement: Q, K, V, O are
+ * [B, H, N, d]) with the masks and LSE described above.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int batch, int heads, int seqlen, int head_dim, int dtype,
+             float softmax_scale, int causal, int window_left, int window_right,
+             void* stream);
+
+/*
+ * attn_fwd_varlen - packed batch of variable-length sequences (self-attention).
+ *   q, k, v, o : [heads, total_tokens, head_dim]
+ *   lse        : [heads, total_tokens] fp32, or NULL
+ *   cu_seqlens : DEVICE int32 array of num_seqs + 1 prefix sums; cu_seqlens[0] = 0,
+ *                nondecreasing, cu_seqlens[num_seqs] = total_tokens.  Sequence s owns tokens
+ *                [cu_seqlens[s], cu_seqlens[s+1]) and attends only within itself (page
+ *                "mainloop_bwd_sm90_tma_gmma_ws.hpp", get_seqlen_q/k: a sequence's length is
+ *                the difference of consecutive cu_seqlens entries).  Zero-length sequences
+ *                are allowed.
+ *   max_seqlen : host upper bound on every sequence length (>= 1 when total_tokens > 0); it
+ *                only sizes the launch, so no device-to-host copy is needed.  A sequence
+ *                longer than max_seqlen is not computed correctly.
+ * num_seqs, total_tokens >= 0 (zero is a no-op).  Masks apply per sequence, as above.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int heads, int head_dim, int dtype, float softmax_scale,
+                    int causal, int window_left, int window_right, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* The hipError_t of the last ATTN_ERR_HIP returned on this thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */
