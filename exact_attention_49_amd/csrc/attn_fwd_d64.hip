@@ -1,0 +1,6 @@
+// Kernel instantiations for head_dim = 64 (all dtypes and mask modes).
+#include "attn_fwd_kernel.h"
+
+namespace xattn {
+XATTN_DEFINE_LAUNCHER(64)
+}  // namespace xattn

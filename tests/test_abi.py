@@ -1,0 +1,107 @@
+"""CPU-side checks of the C-ABI library: it loads, it exports every function the header
+declares, the binding's signatures cover them, and argument validation rejects bad calls on
+the host before any HIP call (no kernel is ever launched here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_49_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exact_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from exact_attention_49_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    assert {"attn_fwd", "attn_fwd_varlen", "attn_status_string"} <= set(fns)
+
+
+def test_library_exports_every_header_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for fn in header_functions():
+        assert fn in exported, fn
+        assert fn in binding.EXPORTED_SYMBOLS, fn
+        assert isinstance(getattr(lib, fn), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS.items():
+        assert lib.attn_status_string(code).decode().startswith(name)
+    assert lib.attn_status_string(12345) == b"unknown status"
+    assert lib.attn_last_hip_error() == 0
+
+
+A = 1 << 20          # a fake, 16-byte aligned address: validation never dereferences it
+SCALE = 0.125
+
+
+def call_dense(lib, q=A, k=A, v=A, o=A, lse=None, b=1, h=1, n=16, d=64, dtype=1,
+               scale=SCALE, causal=0, wl=-1, wr=-1):
+    return lib.attn_fwd(q, k, v, o, lse, b, h, n, d, dtype, scale, causal, wl, wr, None)
+
+
+def call_varlen(lib, q=A, k=A, v=A, o=A, lse=None, cu=A, ns=2, maxs=8, total=16, h=1, d=64,
+                dtype=1, scale=SCALE, causal=0, wl=-1, wr=-1):
+    return lib.attn_fwd_varlen(q, k, v, o, lse, cu, ns, maxs, total, h, d, dtype, scale,
+                               causal, wl, wr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(b=-1), 1), (dict(h=-2), 1), (dict(n=-1), 1),
+    (dict(d=96), 2), (dict(d=32), 2), (dict(d=1024), 2),
+    (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(q=A + 8), 4), (dict(o=A + 2), 4), (dict(lse=A + 2), 4),
+    (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("inf")), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(causal=2), 1), (dict(wl=-2), 1), (dict(wr=-5), 1),
+])
+def test_dense_rejects_bad_arguments(lib, kw, status):
+    assert call_dense(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(h=0), dict(n=0)])
+def test_dense_empty_problem_is_a_no_op(lib, kw):
+    # nothing to compute: returns OK without launching (pointers are never touched)
+    assert call_dense(lib, q=None, k=None, v=None, o=None, **kw) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), 1), (dict(cu=A + 2), 4), (dict(ns=-1), 1), (dict(total=-1), 1),
+    (dict(maxs=0), 1), (dict(maxs=17), 1), (dict(h=-1), 1), (dict(d=80), 2), (dict(dtype=7), 3),
+    (dict(q=None), 1), (dict(v=A + 4), 4), (dict(scale=0.0), 1), (dict(wl=-3), 1),
+])
+def test_varlen_rejects_bad_arguments(lib, kw, status):
+    assert call_varlen(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(ns=0), dict(total=0), dict(h=0)])
+def test_varlen_empty_problem_is_a_no_op(lib, kw):
+    assert call_varlen(lib, q=None, k=None, v=None, o=None, cu=None, **kw) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(binding.AttnError, match="GPU tensor"):
+        binding.attn_fwd(x, x, x)

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
+
+Small shapes are compared in full (they span several q-tiles and K/V tiles plus a ragged
+tail); the five named workloads are compared in full where the oracle is quick and on
+sampled rows (tile boundaries, both ends, random rows) where it is not, plus properties that
+hold at any size."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_49_amd import AttnError, attn_fwd, attn_fwd_varlen, inputs
+from tests.gpu_helpers import (O_TOL, assert_close, gpu_dense, gpu_varlen, oracle_dense,
+                               sample_rows, to64)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+MASKS = {
+    "none": dict(causal=False, wl=-1, wr=-1),
+    "causal": dict(causal=True, wl=-1, wr=-1),
+    "causal_w37": dict(causal=True, wl=37, wr=-1),
+    "window_50_20": dict(causal=False, wl=50, wr=20),
+    "right_only_5": dict(causal=False, wl=-1, wr=5),
+    "left_only_70": dict(causal=False, wl=70, wr=-1),
+}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("dtype", list(DTYPES))
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_dense_small_all_modes(d, dtype, mask):
+    _announce(f"dense d={d} {dtype} {mask}")
+    m = MASKS[mask]
+    q, k, v = inputs.make_dense(2, 2, 300, d, dtype, seed=100 + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu_dense(q, k, v, m["causal"], m["wl"], m["wr"])
+    o_ref, lse_ref = oracle_dense(q, k, v, scale, m["causal"], m["wl"], m["wr"])
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, DTYPES[dtype], f"d={d} {dtype} {mask}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 255, 256, 257, 513])
+@pytest.mark.parametrize("mask", ["none", "causal", "causal_w37"])
+def test_dense_ragged_lengths(n, mask):
+    _announce(f"dense ragged n={n} {mask}")
+    m = MASKS[mask]
+    q, k, v = inputs.make_dense(1, 3, n, 128, "bf16", seed=200 + n)
+    o, lse = gpu_dense(q, k, v, m["causal"], m["wl"], m["wr"])
+    o_ref, lse_ref = oracle_dense(q, k, v, 1 / math.sqrt(128), m["causal"], m["wl"], m["wr"])
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"n={n} {mask}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "causal_w37", "window_50_20"])
+def test_varlen_small(d, mask):
+    _announce(f"varlen small d={d} {mask}")
+    m = MASKS[mask]
+    lens = [1, 0, 64, 300, 1000, 257, 3]
+    q, k, v, cu = inputs.make_varlen(len(lens), 0, 0, 3, d, "bf16", seed=300 + d, lengths=lens)
+    o, lse = gpu_varlen(q, k, v, cu, m["causal"], m["wl"], m["wr"])
+    o_ref, lse_ref = oracle.attention_varlen(q.float().numpy(), k.float().numpy(),
+                                             v.float().numpy(), cu.numpy(), 1 / math.sqrt(d),
+                                             m["causal"], m["wl"], m["wr"])
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"varlen d={d} {mask}")
+
+
+def test_varlen_equals_dense_per_sequence():
+    _announce("varlen == dense per sequence")
+    lens = [129, 700, 5]
+    q, k, v, cu = inputs.make_varlen(3, 0, 0, 2, 128, "fp16", seed=11, lengths=lens)
+    o, lse = gpu_varlen(q, k, v, cu, True, 100, -1)
+    for s, (a, b) in enumerate(zip(cu[:-1].tolist(), cu[1:].tolist())):
+        od, ld = gpu_dense(q[None, :, a:b].contiguous(), k[None, :, a:b].contiguous(),
+                           v[None, :, a:b].contiguous(), True, 100, -1)
+        assert torch.equal(od[0].cpu(), o[:, a:b].cpu()), s
+        assert torch.equal(ld[0].cpu(), lse[:, a:b].cpu()), s
+
+
+# ---------------------------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------------------------
+
+def _dense_workload(name):
+    w = inputs.WORKLOADS[name]
+    q, k, v = inputs.make_workload(w)
+    return w, q, k, v
+
+
+def test_workload_tiny_fp16_d64_full():
+    w, q, k, v = _dense_workload("tiny_fp16_d64")
+    _announce(w.name)
+    o, lse = gpu_dense(q, k, v, w.causal, w.window_left, w.window_right)
+    o_ref, lse_ref = oracle_dense(q, k, v, w.softmax_scale, w.causal, w.window_left,
+                                  w.window_right)
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, w.torch_dtype, w.name)
+
+
+def _check_sampled_dense(w, q, k, v, o, lse, heads, rng):
+    idx = []
+    for (b, h) in heads:
+        idx += [(b, h, r) for r in sample_rows(w.seqlen, rng)]
+    idx = np.array(idx)
+    o_ref, lse_ref = oracle.attention_rows_dense(q.float(), k.float(), v.float(), idx,
+                                                 w.softmax_scale, w.causal, w.window_left,
+                                                 w.window_right)
+    og = o[idx[:, 0], idx[:, 1], idx[:, 2]]
+    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]]
+    return assert_close(to64(og), to64(lg), o_ref, lse_ref, w.torch_dtype, w.name)
+
+
+def _check_finite(o, lse):
+    assert bool(torch.isfinite(o).all()), "non-finite O"
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE"
+
+
+def test_workload_causal_bf16_d128_n2048():
+    w, q, k, v = _dense_workload("causal_bf16_d128_n2048")
+    _announce(w.name)
+    o, lse = gpu_dense(q, k, v, w.causal)
+    o, lse = o.cpu(), lse.cpu()
+    _check_finite(o, lse)
+    # two whole heads in full, then sampled rows of other heads
+    for (b, h) in [(0, 0), (3, 15)]:
+        o_ref, lse_ref = oracle.attention_head(q[b, h].float().numpy(), k[b, h].float().numpy(),
+                                               v[b, h].float().numpy(), w.softmax_scale, True)
+        assert_close(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, w.torch_dtype, w.name)
+    rng = np.random.default_rng(7)
+    _check_sampled_dense(w, q, k, v, o, lse, [(1, 3), (2, 9), (3, 0)], rng)
+
+
+def test_workload_causal_bf16_d128_n8192_sampled():
+    w, q, k, v = _dense_workload("causal_bf16_d128_n8192")
+    _announce(w.name)
+    o, lse = gpu_dense(q, k, v, w.causal)
+    o, lse = o.cpu(), lse.cpu()
+    _check_finite(o, lse)
+    rng = np.random.default_rng(8)
+    _check_sampled_dense(w, q, k, v, o, lse, [(0, 0), (0, 31), (1, 17), (1, 31)], rng)
+
+
+def test_workload_dense_fp16_d512_n4096_sampled():
+    w, q, k, v = _dense_workload("dense_fp16_d512_n4096")
+    _announce(w.name)
+    o, lse = gpu_dense(q, k, v, w.causal)
+    o, lse = o.cpu(), lse.cpu()
+    _check_finite(o, lse)
+    rng = np.random.default_rng(9)
+    _check_sampled_dense(w, q, k, v, o, lse, [(0, 0), (0, 5), (0, 7)], rng)
+
+
+def test_workload_varlen_bf16_d64_w1024_sampled():
+    w = inputs.WORKLOADS["varlen_bf16_d64_w1024"]
+    _announce(w.name)
+    q, k, v, cu = inputs.make_workload(w)
+    o, lse = gpu_varlen(q, k, v, cu, w.causal, w.window_left, w.window_right)
+    o, lse = o.cpu(), lse.cpu()
+    _check_finite(o, lse)
+    rng = np.random.default_rng(10)
+    cu_np = cu.numpy()
+    idx = []
+    for s in range(w.num_seqs):
+        a, b = int(cu_np[s]), int(cu_np[s + 1])
+        h = int(rng.integers(0, w.heads))
+        idx += [(h, a + r) for r in sample_rows(b - a, rng, extra=3)]
+    idx = np.array(idx)
+    o_ref, lse_ref = oracle.attention_rows_varlen(q.float(), k.float(), v.float(), cu_np, idx,
+                                                  w.softmax_scale, w.causal, w.window_left,
+                                                  w.window_right)
+    assert_close(to64(o[idx[:, 0], idx[:, 1]]), to64(lse[idx[:, 0], idx[:, 1]]), o_ref,
+                 lse_ref, w.torch_dtype, w.name)
+
+
+# ---------------------------------------------------------------------------------------------
+# Properties that hold at any size
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mask", ["causal", "causal_w37", "window_50_20"])
+def test_zero_q_gives_log_count(mask):
+    """Q = 0: every visible score is 0, so LSE_i = log(#visible keys of row i) and O_i is the
+    mean of the visible V rows (exact mask geometry at full tile counts)."""
+    _announce(f"zero q {mask}")
+    m = MASKS[mask]
+    n, d = 2048, 128
+    _, k, v = inputs.make_dense(1, 2, n, d, "bf16", seed=12)
+    q = torch.zeros_like(k)
+    o, lse = gpu_dense(q, k, v, m["causal"], m["wl"], m["wr"])
+    vis = oracle.visibility(n, n, m["causal"], m["wl"], m["wr"])
+    cnt = vis.sum(axis=1)
+    assert np.allclose(to64(lse[0, 0]), np.log(cnt), atol=1e-5, rtol=0)
+    vm = v[0, 0].double().numpy()
+    ref = (vis @ vm) / cnt[:, None]
+    assert float(np.max(np.abs(to64(o[0, 0]) - ref))) <= O_TOL[torch.bfloat16]
+
+
+def test_constant_v_gives_constant_output():
+    _announce("constant v")
+    q, k, _ = inputs.make_dense(1, 2, 1000, 128, "fp16", seed=13)
+    v = torch.full_like(q, 0.375)
+    o, _ = gpu_dense(q, k, v, True)
+    # P is rounded to fp16 for the PV product while l sums the fp32 weights, so O is 0.375
+    # up to that rounding, inside the fp16 parity bar
+    assert float((o.cpu().double() - 0.375).abs().max()) <= O_TOL[torch.float16]
+
+
+def test_causal_row_zero_is_v_row_zero():
+    _announce("causal row 0")
+    q, k, v = inputs.make_dense(2, 2, 777, 64, "bf16", seed=14)
+    o, lse = gpu_dense(q, k, v, True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+    s00 = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) * float(np.float32(1 / 8))
+    assert np.allclose(to64(lse[:, :, 0]), s00.numpy(), atol=1e-5)
+
+
+def test_deterministic_and_lse_optional():
+    _announce("determinism")
+    q, k, v = inputs.make_dense(1, 4, 1500, 128, "bf16", seed=15)
+    dev = torch.device("cuda:0")
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o1, l1 = attn_fwd(q, k, v, causal=True)
+    o2, l2 = attn_fwd(q, k, v, causal=True)
+    o3, l3 = attn_fwd(q, k, v, causal=True, return_lse=False)
+    torch.cuda.synchronize()
+    assert l3 is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+
+
+def test_binding_errors_on_gpu_tensors():
+    dev = torch.device("cuda:0")
+    x = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(AttnError, match="HEAD_DIM"):
+        attn_fwd(x, x, x)
+    y = torch.zeros(1, 1, 8, 64, dtype=torch.float32, device=dev)
+    with pytest.raises(AttnError, match="dtype"):
+        attn_fwd(y, y, y)
+    z = torch.zeros(2, 8, 64, dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 8], dtype=torch.int32, device=dev)
+    with pytest.raises(AttnError, match="INVALID_ARG"):
+        attn_fwd_varlen(z, z, z, cu, max_seqlen=9)
