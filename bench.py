@@ -1,0 +1,274 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one forward pass (one attn_fwd / attn_fwd_varlen launch) over the workload's
+inputs, which are resident in HBM before timing starts.  W untimed steps, then exactly K timed
+steps between two device synchronisations.  Rank 0 prints one JSON line:
+
+  value    whole-job TFLOP/s with F = 4*B*H*N^2*d, halved when causal (packed batches count
+           the visible (query, key) pairs: F = 4*H*d*sum_s pairs_s)
+  roofline the dominant (only) kernel against MI355X's dense fp16/bf16 MFMA peak, from the
+           per-launch durations measured with HIP events on the launch stream
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
+
+Other flags: --flush touches 512 MiB between steps (cache-cold timing), --list-workloads,
+--calibrate-copy runs only a plain device copy of known size (for scaling HBM counters).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d, halved if causal) and % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}    # MI355X dense MFMA, AMD's published figure
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "causal_bf16_d128_n8192"
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: recorded HBM counters are only valid for the kernel they
+    were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_49_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(n: int, causal: bool, wl: int, wr: int) -> int:
+    """Exact number of (query, key) pairs with the key visible, for one sequence (Nq = Nk)."""
+    total = 0
+    for i in range(n):
+        lo = 0 if wl < 0 else max(0, i - wl)
+        hi = n - 1
+        if causal:
+            hi = i
+        elif wr >= 0:
+            hi = min(n - 1, i + wr)
+        total += hi - lo + 1
+    return total
+
+
+def workload_flops(w, cu=None) -> float:
+    if w.varlen:
+        lens = (cu[1:] - cu[:-1]).tolist()
+        pairs = sum(visible_pairs(int(n), w.causal, w.window_left, w.window_right) for n in lens)
+        return 4.0 * w.heads * w.head_dim * pairs
+    f = 4.0 * w.batch * w.heads * w.seqlen ** 2 * w.head_dim
+    return f / 2 if w.causal else f
+
+
+def workload_bytes(w, cu=None) -> float:
+    """Algorithmic HBM bytes per launch: Q, K, V read once, O written once (2 B each) and
+    LSE written once (4 B per row)."""
+    rows = w.heads * int(cu[-1]) if w.varlen else w.batch * w.heads * w.seqlen
+    return rows * (4 * w.head_dim * 2 + 4)
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources; else None."""
+    path = os.path.join(TRAFFIC_DIR, f"attn_fwd_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
+    """Time the fp64 oracle on a bounded sample: whole (batch, head) pairs, or whole
+    (sequence, head) pairs for a packed batch, until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    done_flops, t_total, units = 0.0, 0.0, []
+    if w.varlen:
+        cu_l = cu.tolist()
+        order = [(h, s) for s in range(w.num_seqs) for h in range(w.heads)]
+        for (h, s) in order:
+            a, b = cu_l[s], cu_l[s + 1]
+            qs, ks, vs = (x[h, a:b].float().numpy() for x in (q, k, v))
+            t0 = time.perf_counter()
+            oracle.attention_head(qs, ks, vs, w.softmax_scale, w.causal, w.window_left,
+                                  w.window_right)
+            t_total += time.perf_counter() - t0
+            done_flops += 4.0 * w.head_dim * visible_pairs(b - a, w.causal, w.window_left,
+                                                           w.window_right)
+            units.append(f"seq{s}/h{h}")
+            if t_total >= budget_s:
+                break
+        sample = f"{len(units)} (sequence, head) pairs of the packed batch, whole"
+    else:
+        f_head = 4.0 * w.seqlen ** 2 * w.head_dim / (2 if w.causal else 1)
+        for b in range(w.batch):
+            for h in range(w.heads):
+                qs, ks, vs = (x[b, h].float().numpy() for x in (q, k, v))
+                t0 = time.perf_counter()
+                oracle.attention_head(qs, ks, vs, w.softmax_scale, w.causal, w.window_left,
+                                      w.window_right)
+                t_total += time.perf_counter() - t0
+                done_flops += f_head
+                units.append((b, h))
+                if t_total >= budget_s:
+                    break
+            if t_total >= budget_s:
+                break
+        sample = (f"{len(units)} of {w.batch * w.heads} (batch, head) pairs, whole "
+                  f"(N={w.seqlen}, d={w.head_dim}), fp64 numpy")
+    del np
+    return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": sample, "seconds": round(t_total, 2),
+            "host_cpus": os.cpu_count()}
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    import torch
+    dev = torch.device("cuda:0")
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--flush", action="store_true")
+    ap.add_argument("--list-workloads", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    from exact_attention_49_amd import inputs
+    if args.list_workloads:
+        for name, w in inputs.WORKLOADS.items():
+            print(f"{name}: {w.note}")
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(work units are independent per head; see the sharding note in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import torch
+
+    from exact_attention_49_amd import attn_fwd, attn_fwd_varlen
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    cu = None
+    if w.varlen:
+        q, k, v, cu = inputs.make_workload(w)
+        max_len = int((cu[1:] - cu[:-1]).max())
+    else:
+        q, k, v = inputs.make_workload(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    lse_shape = (w.heads, qd.shape[1]) if w.varlen else (w.batch, w.heads, w.seqlen)
+    lsed = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    cud = cu.to(dev) if cu is not None else None
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+
+    def step():
+        if w.varlen:
+            attn_fwd_varlen(qd, kd, vd, cud, max_len, causal=w.causal,
+                            window_left=w.window_left, window_right=w.window_right, out=od,
+                            lse=lsed)
+        else:
+            attn_fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                     window_right=w.window_right, out=od, lse=lsed)
+
+    for _ in range(args.warmup):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    flops = workload_flops(w, cu)
+    algo_bytes = workload_bytes(w, cu)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = load_traffic(w.name)
+
+    config = {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim, "dtype": w.dtype,
+              "causal": w.causal, "window_left": w.window_left,
+              "window_right": w.window_right, "seed": w.seed, "value_scale": w.value_scale}
+    if w.varlen:
+        config.update(num_seqs=w.num_seqs, total_tokens=int(cu[-1]),
+                      lengths=(cu[1:] - cu[:-1]).tolist())
+    else:
+        config.update(batch=w.batch, seqlen=w.seqlen)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, no dataset)", "config": config,
+        "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "flops_per_step": flops, "cache": "flushed 512 MiB between steps" if args.flush
+        else "warm (back-to-back launches)",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_kernel",
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "algorithmic_bytes": algo_bytes,
+                     "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_budget)
+        out["cpu_baseline"]["speedup_gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -6,13 +6,13 @@
 #include <limits>
 
 #include "exact_attn.h"
-#include "attn_fwd_kernel.h"
+#include "attn_dispatch.h"
 
 namespace xattn {
-template <> hipError_t launch_fwd<64>(const FwdArgs&, bool, int, int, hipStream_t);
-template <> hipError_t launch_fwd<128>(const FwdArgs&, bool, int, int, hipStream_t);
-template <> hipError_t launch_fwd<256>(const FwdArgs&, bool, int, int, hipStream_t);
-template <> hipError_t launch_fwd<512>(const FwdArgs&, bool, int, int, hipStream_t);
+template <> hipError_t launch_fwd<64>(const FwdArgs&, bool, int, bool, int, hipStream_t);
+template <> hipError_t launch_fwd<128>(const FwdArgs&, bool, int, bool, int, hipStream_t);
+template <> hipError_t launch_fwd<256>(const FwdArgs&, bool, int, bool, int, hipStream_t);
+template <> hipError_t launch_fwd<512>(const FwdArgs&, bool, int, bool, int, hipStream_t);
 }  // namespace xattn
 
 namespace {
@@ -23,12 +23,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
-int block_rows(int d) {
+// Query rows per workgroup of the big / small tile shape of a head dim.
+int block_rows(int d, bool big) {
   switch (d) {
-    case 64: return xattn::block_rows<64>();
-    case 128: return xattn::block_rows<128>();
-    case 256: return xattn::block_rows<256>();
-    default: return xattn::block_rows<512>();
+    case 64: return big ? xattn::TileCfg<64>::Big::BR : xattn::TileCfg<64>::Small::BR;
+    case 128: return big ? xattn::TileCfg<128>::Big::BR : xattn::TileCfg<128>::Small::BR;
+    case 256: return big ? xattn::TileCfg<256>::Big::BR : xattn::TileCfg<256>::Small::BR;
+    default: return big ? xattn::TileCfg<512>::Big::BR : xattn::TileCfg<512>::Small::BR;
   }
 }
 
@@ -58,7 +59,7 @@ int mask_mode(int causal, int max_len, int* wl, int* wr) {
   return xattn::MASK_WINDOW;
 }
 
-int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, long n_work,
+int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big, long n_work,
            void* stream) {
   if (n_work <= 0) return ATTN_OK;
   if (n_work > std::numeric_limits<int>::max()) return ATTN_ERR_TOO_LARGE;
@@ -66,10 +67,10 @@ int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, long n_wo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   switch (head_dim) {
-    case 64: e = xattn::launch_fwd<64>(a, bf16, mode, (int)n_work, s); break;
-    case 128: e = xattn::launch_fwd<128>(a, bf16, mode, (int)n_work, s); break;
-    case 256: e = xattn::launch_fwd<256>(a, bf16, mode, (int)n_work, s); break;
-    default: e = xattn::launch_fwd<512>(a, bf16, mode, (int)n_work, s); break;
+    case 64: e = xattn::launch_fwd<64>(a, bf16, mode, big, (int)n_work, s); break;
+    case 128: e = xattn::launch_fwd<128>(a, bf16, mode, big, (int)n_work, s); break;
+    case 256: e = xattn::launch_fwd<256>(a, bf16, mode, big, (int)n_work, s); break;
+    default: e = xattn::launch_fwd<512>(a, bf16, mode, big, (int)n_work, s); break;
   }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -101,7 +102,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (rows > kMaxRows) return ATTN_ERR_TOO_LARGE;
   int wl = window_left, wr = window_right;
   const int mode = mask_mode(causal, seqlen, &wl, &wr);
-  const int br = block_rows(head_dim);
+  const bool big = (long)batch * heads * ((seqlen + block_rows(head_dim, true) - 1) /
+                                          block_rows(head_dim, true)) >= xattn::BIG_TILE_MIN_WORK;
+  const int br = block_rows(head_dim, big);
   xattn::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -115,7 +118,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.window_left = wl;
   a.window_right = wr;
   const long n_work = (long)batch * heads * a.tiles_per_head;
-  return launch(head_dim, a, dtype, mode, n_work, stream);
+  return launch(head_dim, a, dtype, mode, big, n_work, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -138,7 +141,10 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   if ((long)heads * total_tokens > kMaxRows) return ATTN_ERR_TOO_LARGE;
   int wl = window_left, wr = window_right;
   const int mode = mask_mode(causal, max_seqlen, &wl, &wr);
-  const int br = block_rows(head_dim);
+  const int br_big = block_rows(head_dim, true);
+  const bool big = (long)heads * (((long)total_tokens + br_big - 1) / br_big) >=
+                   xattn::BIG_TILE_MIN_WORK;
+  const int br = block_rows(head_dim, big);
   // q-tile slots per head: an upper bound on sum_s ceil(len_s / br) that needs no lengths
   const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;
   const long by_max = (long)num_seqs * ((max_seqlen + br - 1) / br);
@@ -158,7 +164,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.scale_log2 = softmax_scale * kLog2e;
   a.window_left = wl;
   a.window_right = wr;
-  return launch(head_dim, a, dtype, mode, (long)heads * slots, stream);
+  return launch(head_dim, a, dtype, mode, big, (long)heads * slots, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -1,0 +1,430 @@
+// Shared pieces of the gfx950 exact-attention forward kernels: argument block, MFMA and
+// conversion wrappers, cross-lane reductions, LDS layout (swizzles), work decoding and the
+// per-tile steps (S^T = K Q^T, mask, online softmax, O^T += V^T P^T, epilogue).
+//
+// What is computed.  For every query row i of a (batch, head) or (sequence, head):
+//   S_ij = scale * q_i . k_j   (keys j visible under the causal / sliding-window mask),
+//   O_i  = sum_j softmax_j(S_ij) v_j,  LSE_i = log sum_j exp(S_ij)  (natural log),
+// by the streaming recurrence of page "flash_attn_mma_tiling_qk.cu" (its KV loop and the
+// "Rescale O" block): per K/V tile keep a running row max m and row sum l,
+//   m_new = max(m, rowmax(S_tile)),  P = exp(S_tile - m_new),  alpha = exp(m - m_new),
+//   l = alpha * l + rowsum(P),  O = alpha * O + P V_tile,
+// and divide O by l at the end.  Masks follow page "mainloop_bwd_sm90_tma_gmma_ws.hpp"
+// (`mma`: causal masking iterations and the Is_local branch) with seqlen_q == seqlen_k:
+// key j is visible to query i iff j <= i + window_right (causal: window_right = 0) and
+// j >= i - window_left (a bound of -1 is unbounded).  A row with no visible key stores
+// O = 0, LSE = -inf (page "flash_fwd_kernel.h" @26a6e0a, consumer loop, store_zero).
+//
+// Register layout (v_mfma_f32_32x32x16, wave64).  The score tile is computed transposed,
+// S^T = K Q^T (the swap-AB idea of page "mainloop_bwd_sm90_tma_gmma_ws.hpp", SdP_swapAB):
+// lane l of a wave owning 32 query rows holds query (l % 32), and accumulator register r of
+// 32-key block kb holds key 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4.  Row max / row sum are
+// therefore in-lane plus one exchange between the two 32-lane halves.  The output is
+// accumulated transposed too, O^T += V^T P^T: the S^T registers converted to 16-bit are the
+// B operand (P^T) as they stand, so P never leaves registers; the matching V^T A operand is
+// read from row-major V in LDS with ds_read_b64_tr_b16.  Register r of 32-wide column block db
+// of O^T holds d = 32 db + 8 (r / 4) + 4 (l / 32) + r % 4 of the lane's own query.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum MaskMode { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2 };
+
+// Kernel arguments (plain data; pointers are device addresses).
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;                 // may be null
+  const int32_t* cu_seqlens;  // null for a dense batch
+  int seqlen;                 // dense: N
+  int num_seqs;               // packed: number of sequences
+  int total_tokens;           // packed: rows per head
+  int tiles_per_head;         // dense: ceil(N / BR); packed: q-tile slots per head
+  float scale_log2;           // softmax_scale * log2(e): scores are exponentiated base 2
+  int window_left;            // -1 = unbounded (MASK_WINDOW only)
+  int window_right;           // -1 = unbounded (MASK_WINDOW only; causal folded in as 0)
+};
+
+// The running max is only moved when a tile's row max exceeds it by more than this (in log2
+// units), so the O rescale is skipped on almost every tile.  The weights exp2(s - m) then stay
+// below 2^8, harmless in fp32 and in the 16-bit P operand, and the result is unchanged: O and
+// l are both taken relative to the same reference m, and LSE = m + log2(l).
+constexpr float RESCALE_SLACK = 8.0f;
+
+// ---------------------------------------------------------------------------------------------
+// Instruction wrappers
+// ---------------------------------------------------------------------------------------------
+
+template <bool BF16> struct Elt;
+template <> struct Elt<true> {
+  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two fp32 -> packed pair, round to nearest even.
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    bf16x2 r = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+template <> struct Elt<false> {
+  static __device__ __forceinline__ f32x16 mfma(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    f16x2 r = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+// Reduce a value across the two 32-lane halves of the wave; both halves get the result.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Workgroup-wide barrier without a memory fence: the compiler may not move memory operations
+// across it, and no wait on outstanding global loads is implied (those are waited for
+// explicitly where the data is needed).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Buffer resource for raw 32-bit-offset loads from `base` (gfx9 family: no stride, dword data
+// format word); `bytes` bounds the range.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  // the descriptor must live in scalar registers: the values are uniform by construction
+  return (i32x4){__builtin_amdgcn_readfirstlane((int)(unsigned)p),
+                 __builtin_amdgcn_readfirstlane((int)((unsigned)(p >> 32) & 0xffffu)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer `rsrc` at voff + soff straight into LDS at lds + 16 * lane
+// (buffer_load ... lds).  Issued as inline assembly so that the compiler's wait-count tracking
+// does not treat later LDS reads as dependent on it; completion is waited for explicitly with
+// wait_vmem() followed by a workgroup barrier.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voff, int soff,
+                                                  const char* lds) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(
+      (__attribute__((address_space(3))) const char*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+// Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroup i is dispatched to XCD i % 8.  Renumber so that XCD x runs the contiguous work
+// range [x * n / 8, (x + 1) * n / 8) (a bijection for any n).
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  constexpr int NX = 8;
+  const int xcd = bid % NX, local = bid / NX;
+  const int per = nwg / NX, rem = nwg % NX;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// LDS swizzles: XOR masks on the 16-byte chunk index of a row.
+//  K is read as the MFMA A operand: 32 consecutive rows, same chunk -> spread rows over all
+//  16 chunk positions of a 256-byte bank window.
+//  V is read by ds_read_b64_tr_b16: 8 consecutive rows x 64 bytes -> move each group of 4
+//  rows to a different 64-byte quarter of the bank window.
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+  return D >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Work decoding
+// ---------------------------------------------------------------------------------------------
+
+struct Work {
+  int tile;    // q-tile index within the sequence
+  int seqlen;  // rows (= keys) of the sequence
+  long row0;   // index of the sequence's token 0 in the [*, D] row space of q/k/v/o and lse
+};
+
+// Map this workgroup to (q-tile, head, batch | sequence).  Dense batches: heads of all batch
+// entries in order, q-tiles of a head consecutive (heaviest first for masked modes, whose
+// later q-tiles see more keys).  Packed batches: the q-tile slots of a head walk the sequences
+// in order; slots past the last tile are unused.  Returns false for an unused slot.
+template <int BR, int MODE>
+__device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.tiles_per_head;
+  if (a.cu_seqlens == nullptr) {
+    const int bh = wid / per, t = wid - bh * per;
+    w.tile = (MODE != MASK_NONE) ? per - 1 - t : t;
+    w.seqlen = a.seqlen;
+    w.row0 = (long)bh * a.seqlen;
+    return true;
+  }
+  const int h = wid / per;
+  const int slot = wid - h * per;
+  int acc = 0;
+  int c_prev = min(max(a.cu_seqlens[0], 0), a.total_tokens);
+  for (int s = 0; s < a.num_seqs; ++s) {
+    // clamped so that malformed prefix sums cannot address outside [0, total_tokens)
+    const int c_next = min(max(a.cu_seqlens[s + 1], c_prev), a.total_tokens);
+    const int nt = (c_next - c_prev + BR - 1) / BR;
+    if (slot < acc + nt) {
+      const int t = slot - acc;
+      w.tile = (MODE != MASK_NONE) ? nt - 1 - t : t;
+      w.seqlen = c_next - c_prev;
+      w.row0 = (long)h * a.total_tokens + c_prev;
+      return true;
+    }
+    acc += nt;
+    c_prev = c_next;
+  }
+  return false;
+}
+
+// Effective window bounds of a mask mode (-1 = unbounded).
+template <int MODE>
+__device__ __forceinline__ void mode_windows(const FwdArgs& a, int& wl, int& wr) {
+  wl = a.window_left;
+  wr = a.window_right;
+  if (MODE == MASK_NONE) { wl = -1; wr = -1; }
+  if (MODE == MASK_CAUSAL) { wl = -1; wr = 0; }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-wave steps on one 32-row query block
+// ---------------------------------------------------------------------------------------------
+
+// Q^T operand fragments: lane holds query `row`, d = 16 c + 8 hh .. + 7 (zeros past the end).
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* qp, int row, int seqlen, int hh,
+                                       i32x4 (&qf)[D / 16]) {
+  const i32x4* src = (const i32x4*)(qp + (long)row * D);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qf[c] = (row < seqlen) ? src[2 * c + hh] : (i32x4){0, 0, 0, 0};
+  // Consume the fragments here, so the wait for these loads sits before the K/V sweep instead
+  // of inside it (where it would also wait for tile loads still in flight).
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
+}
+
+// Per-lane LDS byte offsets of the MFMA operand reads.  The swizzle key of every row a lane
+// reads is the same (it depends only on row bits fixed by the lane), so an operand address is
+// tile base + this lane offset + a compile-time constant (the key block or key chunk), which
+// the compiler folds into the instruction's immediate offset.
+template <int D>
+struct LaneOffsets {
+  int k[D / 16];  // K read of d-chunk c: row l32, 16-byte chunk (2c + hh) swizzled
+  int v[D / 32];  // first V transpose read of column block db (add 8 rows for the second)
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
+  constexpr int ROWB = D * 2;
+  const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4, i16 = lane & 15;
+  LaneOffsets<D> o;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) o.k[c] = l32 * ROWB + (((2 * c + hh) ^ swz_k<D>(l32)) << 4);
+  const int vrow = 4 * (g >> 1) + (i16 >> 2);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+    o.v[db] = vrow * ROWB + (((col >> 3) ^ swz_v<D>(vrow)) << 4) + ((col & 7) << 1);
+  }
+  return o;
+}
+
+// Keeps the compiler from moving instructions across this point, so that operand reads stay
+// ahead of the MFMAs that consume them.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// S^T[key, query] = sum_d K[key, d] Q[query, d] for the BC keys of an LDS K tile.  Steps go
+// d-chunk by d-chunk, alternating the 32-key blocks (independent accumulators); the K operand
+// of step i + PF - 1 is read before the MFMA of step i.
+template <bool BF16, int D, int BC, int PF = 3>
+__device__ __forceinline__ void mma_scores(const char* kt, const LaneOffsets<D>& lo,
+                                           const i32x4 (&qf)[D / 16], f32x16 (&s)[BC / 32]) {
+  constexpr int ROWB = D * 2, KB = BC / 32, N = (D / 16) * KB;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  auto read = [&](int i) {
+    const int c = i / KB, kb = i % KB;
+    return *(const i32x4*)(kt + lo.k[c] + kb * 32 * ROWB);
+  };
+  i32x4 buf[PF];
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) buf[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
+    sched_fence();
+    s[i % KB] = Elt<BF16>::mfma(buf[i % PF], qf[i / KB], s[i % KB]);
+    sched_fence();
+  }
+}
+
+// Set invisible scores to -inf: key k0 + (tile position) against query qrow.
+template <int BC>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[BC / 32], int k0, int qrow, int seqlen,
+                                            int wl, int wr, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool vis = key < seqlen && (wr < 0 || key <= qrow + wr) &&
+                       (wl < 0 || key >= qrow - wl);
+      if (!vis) s[kb][r] = -INFINITY;
+    }
+}
+
+// Online softmax of one tile (base 2) with a lazily moved reference max.  Turns the scores
+// into P packed to 16-bit (the B operand of O^T += V^T P^T), updates m and the lane's partial
+// l, and returns the factor O must be multiplied by (1 unless the reference max moved).
+// `moved` tells whether any row of the lane moved it.
+template <bool BF16, int BC>
+__device__ __forceinline__ float softmax_tile(f32x16 (&s)[BC / 32], i32x4 (&pf)[BC / 16],
+                                              float c2, float& m_run, float& l_run,
+                                              bool& moved) {
+  // Row max and row sum over the lane's BC / 2 scores use NP independent partial chains: the
+  // serial chain of dependent max / add instructions is what bounds this step otherwise.
+  constexpr int NP = 4;
+  float pm[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) pm[k] = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pm[r % NP] = fmaxf(pm[r % NP], s[kb][r]);
+  float mx = fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]));
+  mx = halves_max(mx) * c2;                          // this tile's row max, log2 units
+  const bool move = mx > m_run + RESCALE_SLACK;      // false while both are -inf
+  const float m_new = move ? mx : m_run;
+  // a row with nothing visible so far keeps m = -inf; subtract 0 so exp2 gives 0, not NaN
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = move ? fast_exp2(m_run - m_use) : 1.f;
+  float ps[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) ps[k] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(s[kb][r], c2, -m_use));
+      s[kb][r] = e;
+      ps[r % NP] += e;
+    }
+  const float rs = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  l_run = fmaf(l_run, alpha, rs);  // per-lane partial; the two halves are summed at the end
+  m_run = m_new;
+  moved = move;
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc) {
+    const int kb = kc >> 1, o8 = (kc & 1) * 8;
+    pf[kc] = (i32x4){(int)Elt<BF16>::pack2(s[kb][o8 + 0], s[kb][o8 + 1]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 4], s[kb][o8 + 5]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
+  }
+  return alpha;
+}
+
+template <int D>
+__device__ __forceinline__ void scale_o(f32x16 (&o)[D / 32], float alpha) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+}
+
+// O^T[d, query] += sum_key V[key, d] P[query, key] for the BC keys of an LDS V tile.  The A
+// operand (V^T) for lane l is column d = 32 db + l % 32, keys 16 kc + 4 hh + {0..3} and
+// 16 kc + 8 + 4 hh + {0..3}: the key slots the S^T accumulator gave P.  Two transpose reads
+// fetch them.  Steps alternate the column blocks (independent accumulators); the operand of
+// step i + PF - 1 is read before the MFMA of step i.
+template <bool BF16, int D, int BC, int PF = 3>
+__device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
+                                       const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32]) {
+  constexpr int ROWB = D * 2, DB = D / 32, N = (BC / 16) * DB;
+  auto read = [&](int i) {
+    const int kc = i / DB, db = i % DB;
+    const char* p = vt + lo.v[db] + 16 * kc * ROWB;
+    const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
+    const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p + 8 * ROWB));
+    return (i32x4){a[0], a[1], b[0], b[1]};
+  };
+  i32x4 buf[PF];
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) buf[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
+    sched_fence();
+    o[i % DB] = Elt<BF16>::mfma(buf[i % PF], pf[i / DB], o[i % DB]);
+    sched_fence();
+  }
+}
+
+// Epilogue for one 32-row block: O = O / l (16-bit, round to nearest even) and
+// LSE = (m + log2 l) ln 2.  All lanes must call it (cross-half sum); rows past the end of the
+// sequence are not stored.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rows(const FwdArgs& a, long row0, int qrow, int seqlen,
+                                           int hh, const f32x16 (&o)[D / 32], float m_run,
+                                           float l_run) {
+  constexpr float LN2 = 0.693147180559945309f;
+  const float lt = halves_sum(l_run);
+  if (qrow >= seqlen) return;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  uint16_t* dst = a.o + (row0 + qrow) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& x = o[db];
+      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
+                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
+      *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
+    }
+  if (a.lse != nullptr && hh == 0)
+    a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
+}
+
+}  // namespace xattn

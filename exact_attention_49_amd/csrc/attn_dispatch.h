@@ -1,0 +1,85 @@
+// Kernel selection and launch for the exact-attention forward: one tile shape per head dim for
+// grids that fill the chip several times over ("big") and one with fewer rows per workgroup
+// for small grids.  Shapes were chosen by measurement on MI355X.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_fwd_kernel.h"
+#include "attn_fwd_pingpong.h"
+
+namespace xattn {
+
+// Shape tags: the ping-pong kernel, or the generic kernel with a Tile shape.
+struct UsePingPong {
+  static constexpr int BR = PingPongShape::BR;
+};
+template <class T> struct UseGeneric {
+  static constexpr int BR = T::BR;
+};
+
+template <int D> struct TileCfg;
+template <> struct TileCfg<64> {
+  using Big = UsePingPong;
+  using Small = UseGeneric<Tile<4, 64, 2, 3>>;
+};
+template <> struct TileCfg<128> {
+  using Big = UsePingPong;
+  using Small = UseGeneric<Tile<4, 64, 2, 2>>;
+};
+template <> struct TileCfg<256> {
+  using Big = UseGeneric<Tile<4, 32, 2, 1>>;
+  using Small = Big;
+};
+template <> struct TileCfg<512> {
+  using Big = UseGeneric<Tile<4, 32, 1, 1>>;
+  using Small = Big;
+};
+
+// Workgroups the big shape must yield before it is preferred (4 per CU on 256 CUs).
+constexpr long BIG_TILE_MIN_WORK = 1024;
+
+template <bool BF16, int D, int MODE, class S> struct Launch;
+template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong> {
+  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_pp_kernel<BF16, D, MODE>), dim3(n_work),
+                       dim3(PingPongShape::NT), 0, s, a);
+  }
+};
+template <bool BF16, int D, int MODE, class T> struct Launch<BF16, D, MODE, UseGeneric<T>> {
+  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, MODE, T>), dim3(n_work), dim3(T::NT), 0, s,
+                       a);
+  }
+};
+
+template <int D, class S>
+hipError_t launch_shape(const FwdArgs& a, bool bf16, int mode, int n_work, hipStream_t s) {
+  if (bf16) {
+    if (mode == MASK_NONE) Launch<true, D, MASK_NONE, S>::go(a, n_work, s);
+    else if (mode == MASK_CAUSAL) Launch<true, D, MASK_CAUSAL, S>::go(a, n_work, s);
+    else Launch<true, D, MASK_WINDOW, S>::go(a, n_work, s);
+  } else {
+    if (mode == MASK_NONE) Launch<false, D, MASK_NONE, S>::go(a, n_work, s);
+    else if (mode == MASK_CAUSAL) Launch<false, D, MASK_CAUSAL, S>::go(a, n_work, s);
+    else Launch<false, D, MASK_WINDOW, S>::go(a, n_work, s);
+  }
+  return hipGetLastError();
+}
+
+// Host launcher for one head dim (explicitly specialised per head dim in its own translation
+// unit).  `big` selects the shape; the caller sizes the grid with that shape's BR.
+template <int D>
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int mode, bool big, int n_work,
+                      hipStream_t stream);
+
+#define XATTN_DEFINE_LAUNCHER(D)                                                            \
+  template <>                                                                               \
+  hipError_t launch_fwd<D>(const FwdArgs& a, bool bf16, int mode, bool big, int n_work,     \
+                           hipStream_t stream) {                                            \
+    if (big || std::is_same<TileCfg<D>::Big, TileCfg<D>::Small>::value)                     \
+      return launch_shape<D, TileCfg<D>::Big>(a, bf16, mode, n_work, stream);               \
+    return launch_shape<D, TileCfg<D>::Small>(a, bf16, mode, n_work, stream);               \
+  }
+
+}  // namespace xattn

@@ -1,5 +1,5 @@
 // Kernel instantiations for head_dim = 512 (all dtypes and mask modes).
-#include "attn_fwd_kernel.h"
+#include "attn_dispatch.h"
 
 namespace xattn {
 XATTN_DEFINE_LAUNCHER(512)

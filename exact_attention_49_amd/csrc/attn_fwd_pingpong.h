@@ -1,0 +1,203 @@
+// Ping-pong exact-attention forward kernel for gfx950 (head dims 64 and 128).
+//
+// A workgroup is 8 waves of 32 query rows (256 rows of one (batch|sequence, head)); the waves
+// are split into two groups of four, A (waves 0-3) and B (waves 4-7), so that each SIMD runs
+// one wave of each.  Per K/V tile a wave does three steps: S = K Q^T (MFMA), the online softmax
+// (VALU + transcendental) and O += V^T P^T (MFMA).  Grouped as
+//     MFMA block j:  O += V_j^T P_j^T  and  S_{j+1} = K_{j+1} Q^T
+//     VALU block j:  softmax of S_j -> P_j
+// group B runs half a tile behind group A: while A's waves issue their MFMA block, B's waves
+// run their softmax on the same SIMDs, and the other way round.  Two workgroup barriers per
+// tile keep the two groups in step.  This is the producer/consumer overlap of the Hopper
+// kernels on page "flash_fwd_kernel.h" (@26a6e0a, the MMA warpgroups working while others do
+// softmax) realised with wave64 barriers instead of warpgroup specialisation.
+//
+// K and V tiles (64 keys) are loaded by group B during its softmax half, straight from global
+// memory into LDS (global_load_lds_dwordx4: lane l writes LDS base + 16 l, so the XOR swizzle
+// is applied by choosing which 16-byte chunk each lane fetches).  A tile has two half-phases
+// to arrive before it is read; buffers are double-buffered per matrix.  Rows past the end of
+// the sequence fetch the last valid row instead (finite data; those keys are masked to -inf,
+// so they contribute exactly 0).
+//
+// Half-phase schedule (h counts barriers; U_u = {V_u, K_{u+1}} lives in buffer u & 1):
+//   h = 2j   : A softmax(j)              | B  O += V_{j-1} P_{j-1}, S_j = K_j Q^T
+//   h = 2j+1 : A  O += V_j P_j, S_{j+1}  | B softmax(j), and B issues the loads of U_{j+1}
+//   B waits for its loads of U_j at the end of h = 2j; the barrier then publishes them.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace xattn {
+
+struct PingPongShape {
+  static constexpr int NW = 8, NT = 512, BR = 256, BC = 64;
+};
+
+template <bool BF16, int D, int MODE, int PF = 3>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_pp_kernel(FwdArgs a) {
+  constexpr int BR = PingPongShape::BR, BC = PingPongShape::BC;
+  constexpr int CH = D / 8;                     // 16-byte chunks per row
+  constexpr int TILEB = BC * D * 2;             // bytes per K (or V) tile
+  constexpr int LOADERS = 4;                    // group B's waves issue the tile loads
+  constexpr int LI = BC * CH / (LOADERS * 64);  // load instructions per matrix per loader wave
+  static_assert(BC * CH % (LOADERS * 64) == 0, "tile must split evenly over the loader waves");
+  static_assert(D == 64 || D == 128, "ping-pong shape is for head dims 64 and 128");
+
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const bool grp_a = wave < 4;
+
+  Work w;
+  if (!decode_work<BR, MODE>(a, w)) return;
+  const int seqlen = w.seqlen;
+  int wl, wr;
+  mode_windows<MODE>(a, wl, wr);
+
+  const int q0 = w.tile * BR;
+  const int qw0 = q0 + wave * 32;                      // first row of this wave
+  const int q_last = min(q0 + BR, seqlen) - 1;         // last valid row of the workgroup
+  int k_lo = 0, k_hi = seqlen - 1;                     // keys any valid row can see
+  if (wl >= 0) k_lo = max(0, q0 - wl);
+  if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
+  const int t_lo = k_lo / BC;
+  const int n = k_hi / BC - t_lo + 1;                  // K/V tiles to sweep (>= 1)
+
+  const bool wave_active = qw0 < seqlen;
+  const int qw_last = min(qw0 + 32, seqlen) - 1;
+  int kw_lo = 0, kw_hi = seqlen - 1;                   // keys this wave's rows can see
+  if (wl >= 0) kw_lo = max(0, qw0 - wl);
+  if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
+
+  const uint16_t* __restrict__ kp = a.k + w.row0 * D;
+  const uint16_t* __restrict__ vp = a.v + w.row0 * D;
+  const int qrow = qw0 + l32;
+
+  i32x4 qf[D / 16];
+  load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+  f32x16 sacc[BC / 32];  // S^T of the tile between its MFMA block and its softmax
+  i32x4 pf[BC / 16];     // P of the tile between its softmax and its MFMA block
+
+  // ---- direct global -> LDS tile loads (group B only) ------------------------------------
+  // Loader wave lw, instruction i fills LDS 16-byte slots (i * LOADERS + lw) * 64 + lane.  Slot
+  // p holds row p / CH, chunk (p % CH) ^ swizzle(row); since LOADERS * 64 / CH rows is a whole
+  // number of swizzle periods, instruction i reads the bytes of instruction 0 shifted by
+  // i * 4096, so one per-lane offset serves all of them (the shift goes to the scalar offset).
+  const int lw = wave - 4;  // loader index within group B
+  static_assert((LOADERS * 64 / CH) % 16 == 0, "loader rows must cover whole swizzle periods");
+  const int lrow = (lw * 64 + lane) / CH;  // row of this lane's slot in instruction 0
+  const int lch = (lw * 64 + lane) % CH;
+  const int voff_k = lrow * D * 2 + ((lch ^ swz_k<D>(lrow)) << 4);
+  const int voff_v = lrow * D * 2 + ((lch ^ swz_v<D>(lrow)) << 4);
+  const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * D * 2);
+  const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * D * 2);
+  constexpr int ISTEP = LOADERS * 64 * 16;  // bytes per load instruction (all loader waves)
+  auto load_tile = [&](const i32x4& rsrc, int voff0, int swz_shift_k, int r, char* dst) {
+    const int kbase = (t_lo + r) * BC;
+    if (kbase + BC <= seqlen) {
+#pragma unroll
+      for (int i = 0; i < LI; ++i)
+        buffer_load_lds16(rsrc, voff0, kbase * D * 2 + i * ISTEP, dst + i * ISTEP + lw * 1024);
+    } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
+#pragma unroll
+      for (int i = 0; i < LI; ++i) {
+        const int row = lrow + i * (LOADERS * 64 / CH);
+        const int crow = min(row, seqlen - 1 - kbase);
+        const int sw = swz_shift_k ? swz_k<D>(row) : swz_v<D>(row);
+        buffer_load_lds16(rsrc, crow * D * 2 + ((lch ^ sw) << 4), kbase * D * 2,
+                          dst + i * ISTEP + lw * 1024);
+      }
+    }
+  };
+  auto load_k = [&](int r, char* dst) { load_tile(rsrc_k, voff_k, 1, r, dst); };
+  auto load_v = [&](int r, char* dst) { load_tile(rsrc_v, voff_v, 0, r, dst); };
+
+  // ---- the three per-tile steps of a wave (r = tile index relative to t_lo) ---------------
+  auto sees = [&](int r) {
+    const int k0 = (t_lo + r) * BC;
+    return wave_active && k0 <= kw_hi && k0 + BC - 1 >= kw_lo;
+  };
+  auto step_scores = [&](int r, const char* kt) {
+    if (sees(r)) mma_scores<BF16, D, BC, PF>(kt, lo, qf, sacc);
+  };
+  auto step_softmax = [&](int r) {
+    if (!sees(r)) return;
+    const int k0 = (t_lo + r) * BC;
+    const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
+                           (wl >= 0 && k0 < qw0 + 31 - wl);
+    if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+    bool moved;
+    const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
+  };
+  auto step_pv = [&](int r, const char* vt) {
+    if (sees(r)) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
+  };
+
+  // ---- prologue: K_0 (buffer 1), V_0 and K_1 (buffer 0) ---------------------------------
+  if (!grp_a) {
+    load_k(0, k_lds1);
+    load_v(0, v_lds0);
+    if (n > 1) load_k(1, k_lds0);
+    wait_vmem();
+  }
+  block_barrier();
+  if (grp_a) step_scores(0, k_lds1);
+
+  // ---- main loop: two half-phases per tile, buffer parity P = j & 1 known at compile time ----
+  auto iteration = [&](int j, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    char* const kP = P ? k_lds1 : k_lds0;  // holds K_{j+1}
+    char* const kQ = P ? k_lds0 : k_lds1;  // holds K_j, then receives K_{j+2}
+    char* const vP = P ? v_lds1 : v_lds0;  // holds V_j
+    char* const vQ = P ? v_lds0 : v_lds1;  // holds V_{j-1}, then receives V_{j+1}
+    // half-phase 2j
+    if (grp_a) {
+      if (j < n) step_softmax(j);
+    } else {
+      if (j >= 1) step_pv(j - 1, vQ);
+      if (j < n) step_scores(j, kQ);
+    }
+    if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
+    block_barrier();
+    // half-phase 2j+1
+    if (!grp_a && j + 1 < n) {
+      if (j + 2 < n) load_k(j + 2, kQ);
+      load_v(j + 1, vQ);
+    }
+    if (grp_a) {
+      if (j < n) {
+        step_pv(j, vP);
+        if (j + 1 < n) step_scores(j + 1, kP);
+      }
+    } else {
+      if (j < n) step_softmax(j);
+    }
+    block_barrier();
+  };
+  for (int j = 0; j <= n; j += 2) {
+    iteration(j, std::integral_constant<int, 0>{});
+    if (j + 1 <= n) iteration(j + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (wave_active) store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+}
+
+}  // namespace xattn
