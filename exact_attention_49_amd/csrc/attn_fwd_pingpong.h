@@ -172,8 +172,10 @@ void attn_fwd_pp_kernel(FwdArgs a) {
     if (grp_a) {
       if (j < n) step_softmax(j);
     } else {
+      __builtin_amdgcn_s_setprio(2);  // MFMA block: win issue over the partner's softmax
       if (j >= 1) step_pv(j - 1, vQ);
       if (j < n) step_scores(j, kQ);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
     block_barrier();
@@ -183,10 +185,12 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       load_v(j + 1, vQ);
     }
     if (grp_a) {
+      __builtin_amdgcn_s_setprio(2);
       if (j < n) {
         step_pv(j, vP);
         if (j + 1 < n) step_scores(j + 1, kP);
       }
+      __builtin_amdgcn_s_setprio(0);
     } else {
       if (j < n) step_softmax(j);
     }
