@@ -30,9 +30,16 @@ CFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# The wide-head-dim kernels keep the output accumulators in AGPRs through inline assembly and
+# want every compiler-selected MFMA in VGPR form.
+EXTRA_FLAGS = {
+    "attn_fwd_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+    "attn_fwd_d512.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
 
 def _compile(src: str, obj: str) -> str:
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in (r.stderr or "").splitlines() if noise not in x)

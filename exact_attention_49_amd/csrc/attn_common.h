@@ -134,14 +134,28 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
 // 16 bytes per lane from buffer `rsrc` at voff + soff straight into LDS at lds + 16 * lane
 // (buffer_load ... lds).  Issued as inline assembly so that the compiler's wait-count tracking
 // does not treat later LDS reads as dependent on it; completion is waited for explicitly with
-// wait_vmem() followed by a workgroup barrier.
+// wait_vmem() followed by a workgroup barrier.  The LDS address goes through M0, whose previous
+// value is restored.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voff, int soff,
+                                                  unsigned lds_addr) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds_addr);
+  int saved;  // M0 is reserved by the compiler: restore whatever it held
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(unsigned long long)((__attribute__((address_space(3))) const char*)p);
+}
+
 __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voff, int soff,
                                                   const char* lds) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(
-      (__attribute__((address_space(3))) const char*)lds));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory", "m0");
+  buffer_load_lds16(rsrc, voff, soff, lds_address(lds));
 }
 
 // Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
@@ -244,13 +258,24 @@ __device__ __forceinline__ void load_q(const uint16_t* qp, int row, int seqlen, 
 }
 
 // Per-lane LDS byte offsets of the MFMA operand reads.  The swizzle key of every row a lane
-// reads is the same (it depends only on row bits fixed by the lane), so an operand address is
-// tile base + this lane offset + a compile-time constant (the key block or key chunk), which
-// the compiler folds into the instruction's immediate offset.
+// reads is the same (it depends only on row bits fixed by the lane), and it only permutes the
+// low four (K) or the bits 2-3 (V) of the 16-byte chunk index.  So an operand address is tile
+// base + one of a few lane offsets + a compile-time constant (key block, key chunk, and the
+// 256-byte group of the d-chunk), which the compiler folds into the immediate offset.
 template <int D>
 struct LaneOffsets {
-  int k[D / 16];  // K read of d-chunk c: row l32, 16-byte chunk (2c + hh) swizzled
-  int v[D / 32];  // first V transpose read of column block db (add 8 rows for the second)
+  static constexpr int NK = D / 16 < 8 ? D / 16 : 8;  // distinct K offsets (d-chunks mod 8)
+  static constexpr int NV = D / 32 < 4 ? D / 32 : 4;  // distinct V offsets (column blocks mod 4)
+  int k[NK];  // K read of d-chunk c: row l32, 16-byte chunk (2c + hh) swizzled
+  int v[NV];  // first V transpose read of column block db (add 8 rows for the second)
+  // byte offset (within a tile) of the K operand of d-chunk c and 32-key block kb
+  __device__ __forceinline__ int kofs(int c, int kb) const {
+    return k[c % NK] + (c / NK) * 256 + kb * 32 * D * 2;
+  }
+  // byte offset of the first V transpose read of column block db and 16-key chunk kc
+  __device__ __forceinline__ int vofs(int db, int kc) const {
+    return v[db % NV] + (db / NV) * 256 + 16 * kc * D * 2;
+  }
 };
 
 template <int D>
@@ -259,10 +284,11 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4, i16 = lane & 15;
   LaneOffsets<D> o;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) o.k[c] = l32 * ROWB + (((2 * c + hh) ^ swz_k<D>(l32)) << 4);
+  for (int c = 0; c < LaneOffsets<D>::NK; ++c)
+    o.k[c] = l32 * ROWB + (((2 * c + hh) ^ swz_k<D>(l32)) << 4);
   const int vrow = 4 * (g >> 1) + (i16 >> 2);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < LaneOffsets<D>::NV; ++db) {
     const int col = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
     o.v[db] = vrow * ROWB + (((col >> 3) ^ swz_v<D>(vrow)) << 4) + ((col & 7) << 1);
   }
@@ -279,14 +305,13 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 template <bool BF16, int D, int BC, int PF = 3>
 __device__ __forceinline__ void mma_scores(const char* kt, const LaneOffsets<D>& lo,
                                            const i32x4 (&qf)[D / 16], f32x16 (&s)[BC / 32]) {
-  constexpr int ROWB = D * 2, KB = BC / 32, N = (D / 16) * KB;
+  constexpr int KB = BC / 32, N = (D / 16) * KB;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
   auto read = [&](int i) {
-    const int c = i / KB, kb = i % KB;
-    return *(const i32x4*)(kt + lo.k[c] + kb * 32 * ROWB);
+    return *(const i32x4*)(kt + lo.kofs(i / KB, i % KB));
   };
   i32x4 buf[PF];
 #pragma unroll
@@ -384,8 +409,7 @@ __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
                                        const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32]) {
   constexpr int ROWB = D * 2, DB = D / 32, N = (BC / 16) * DB;
   auto read = [&](int i) {
-    const int kc = i / DB, db = i % DB;
-    const char* p = vt + lo.v[db] + 16 * kc * ROWB;
+    const char* p = vt + lo.vofs(i % DB, i / DB);
     const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
     const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p + 8 * ROWB));
     return (i32x4){a[0], a[1], b[0], b[1]};

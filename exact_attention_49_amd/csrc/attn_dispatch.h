@@ -7,12 +7,17 @@
 
 #include "attn_fwd_kernel.h"
 #include "attn_fwd_pingpong.h"
+#include "attn_fwd_wide.h"
 
 namespace xattn {
 
-// Shape tags: the ping-pong kernel, or the generic kernel with a Tile shape.
+// Shape tags: the ping-pong kernel, the wide-head-dim kernel, or the generic kernel with a
+// Tile shape.
 struct UsePingPong {
   static constexpr int BR = PingPongShape::BR;
+};
+struct UseWide {
+  static constexpr int BR = WideShape::BR;
 };
 template <class T> struct UseGeneric {
   static constexpr int BR = T::BR;
@@ -28,11 +33,11 @@ template <> struct TileCfg<128> {
   using Small = UseGeneric<Tile<4, 64, 2, 2>>;
 };
 template <> struct TileCfg<256> {
-  using Big = UseGeneric<Tile<4, 32, 2, 1>>;
+  using Big = UseWide;
   using Small = Big;
 };
 template <> struct TileCfg<512> {
-  using Big = UseGeneric<Tile<4, 32, 1, 1>>;
+  using Big = UseWide;
   using Small = Big;
 };
 
@@ -44,6 +49,12 @@ template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong> 
   static void go(const FwdArgs& a, int n_work, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_pp_kernel<BF16, D, MODE>), dim3(n_work),
                        dim3(PingPongShape::NT), 0, s, a);
+  }
+};
+template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UseWide> {
+  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<BF16, D, MODE>), dim3(n_work), dim3(WideShape::NT),
+                       0, s, a);
   }
 };
 template <bool BF16, int D, int MODE, class T> struct Launch<BF16, D, MODE, UseGeneric<T>> {
