@@ -79,17 +79,38 @@ def workload_bytes(w, cu=None) -> float:
     return rows * (4 * w.head_dim * 2 + 4)
 
 
+def kernel_name(w, cu=None) -> str:
+    """The kernel the library launches for a workload (mirrors the host dispatch: the wide
+    kernel for d >= 256; for d <= 128 the ping-pong kernel once the grid of 256-row tiles has
+    at least 1024 workgroups, else the generic one)."""
+    if w.head_dim >= 256:
+        return "attn_fwd_wide_kernel"
+    if w.varlen:
+        tiles = w.heads * ((int(cu[-1]) + 255) // 256)
+    else:
+        tiles = w.batch * w.heads * ((w.seqlen + 255) // 256)
+    return "attn_fwd_pp_kernel" if tiles >= 1024 else "attn_fwd_kernel"
+
+
 def load_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
-    current kernel sources; else None."""
-    path = os.path.join(TRAFFIC_DIR, f"attn_fwd_{workload}_hbm_traffic.json")
+    """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE,
+    scaled by a plain copy's readings), if they were taken on the current kernel sources;
+    else None.  The summary holds `key: value` lines."""
+    path = os.path.join(TRAFFIC_DIR, f"attn_fwd_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep:
+                rec[key.strip()] = val.strip()
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
@@ -257,7 +278,7 @@ def main() -> int:
         else "warm (back-to-back launches)",
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel": "attn_fwd_kernel",
+                     "traffic": traffic, "kernel": kernel_name(w, cu),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
