@@ -81,6 +81,8 @@ int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big,
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr long kMaxRows = 1L << 40;  // rows * head_dim stays far inside int64
+// The kernels address one sequence's K/V rows with 32-bit byte offsets (buffer loads).
+constexpr long kMaxSeqBytes = (1L << 31) - 1;
 
 }  // namespace
 
@@ -100,6 +102,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                         window_right);
   if (st != ATTN_OK) return st;
   if (rows > kMaxRows) return ATTN_ERR_TOO_LARGE;
+  if ((long)seqlen * head_dim * 2 > kMaxSeqBytes) return ATTN_ERR_TOO_LARGE;
   int wl = window_left, wr = window_right;
   const int mode = mask_mode(causal, seqlen, &wl, &wr);
   const bool big = (long)batch * heads * ((seqlen + block_rows(head_dim, true) - 1) /
@@ -139,6 +142,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   if (!aligned(cu_seqlens, 4)) return ATTN_ERR_MISALIGNED;
   if (max_seqlen < 1 || max_seqlen > total_tokens) return ATTN_ERR_INVALID_ARG;
   if ((long)heads * total_tokens > kMaxRows) return ATTN_ERR_TOO_LARGE;
+  if ((long)max_seqlen * head_dim * 2 > kMaxSeqBytes) return ATTN_ERR_TOO_LARGE;
   int wl = window_left, wr = window_right;
   const int mode = mask_mode(causal, max_seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);

@@ -28,7 +28,8 @@
  *     fail validation.  Arguments are validated on the host only: the contents of device
  *     arrays (cu_seqlens) are trusted.
  *   - Supported head_dim: 64, 128, 256, 512.  Supported dtype: ATTN_DTYPE_FP16,
- *     ATTN_DTYPE_BF16.  Any sequence length is accepted (no tile-multiple requirement).
+ *     ATTN_DTYPE_BF16.  Any sequence length is accepted (no tile-multiple requirement) up to
+ *     seqlen * head_dim * 2 < 2^31 bytes per (sequence, head) (ATTN_ERR_TOO_LARGE beyond).
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H

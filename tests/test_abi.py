@@ -75,6 +75,8 @@ def call_varlen(lib, q=A, k=A, v=A, o=A, lse=None, cu=A, ns=2, maxs=8, total=16,
     (dict(scale=0.0), 1), (dict(scale=-1.0), 1), (dict(scale=float("inf")), 1),
     (dict(scale=float("nan")), 1),
     (dict(causal=2), 1), (dict(wl=-2), 1), (dict(wr=-5), 1),
+    # one (sequence, head) of K or V must stay below 2 GiB (32-bit byte offsets)
+    (dict(n=1 << 21, d=512), 5), (dict(n=1 << 23, d=128), 5),
 ])
 def test_dense_rejects_bad_arguments(lib, kw, status):
     assert call_dense(lib, **kw) == status
@@ -90,6 +92,7 @@ def test_dense_empty_problem_is_a_no_op(lib, kw):
     (dict(cu=None), 1), (dict(cu=A + 2), 4), (dict(ns=-1), 1), (dict(total=-1), 1),
     (dict(maxs=0), 1), (dict(maxs=17), 1), (dict(h=-1), 1), (dict(d=80), 2), (dict(dtype=7), 3),
     (dict(q=None), 1), (dict(v=A + 4), 4), (dict(scale=0.0), 1), (dict(wl=-3), 1),
+    (dict(maxs=1 << 21, total=1 << 21, d=512), 5),
 ])
 def test_varlen_rejects_bad_arguments(lib, kw, status):
     assert call_varlen(lib, **kw) == status
