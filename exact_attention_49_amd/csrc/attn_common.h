@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace xattn {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -146,6 +148,25 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, int voff, int soff
       : "=&s"(saved)
       : "s"(m0), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
+}
+
+// As above, with compile-time byte offsets added in scalar registers inside the instruction
+// sequence: LDS address lds_base + LDS_IMM, global offset voff + soff + G_IMM.  Keeps the
+// per-instruction constants out of live scalar registers.
+template <int LDS_IMM, int G_IMM>
+__device__ __forceinline__ void buffer_load_lds16_at(i32x4 rsrc, int voff, int soff,
+                                                     unsigned lds_base) {
+  int saved, so;
+  // the descriptor is uniform by construction; say so, so that it stays in scalar registers
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_add_u32 m0, %2, %6\n\ts_add_u32 %1, %5, %7\n\t"
+      "buffer_load_dwordx4 %3, %4, %1 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved), "=&s"(so)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rs),
+        "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(LDS_IMM), "n"(G_IMM)
+      : "memory", "scc");
 }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -295,59 +316,95 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   return o;
 }
 
+// Lambdas that must be inlined (the kernels rely on every array staying in registers).
+#define XATTN_INLINE __attribute__((always_inline))
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Keeps the compiler from moving instructions across this point, so that operand reads stay
 // ahead of the MFMAs that consume them.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // S^T[key, query] = sum_d K[key, d] Q[query, d] for the BC keys of an LDS K tile.  Steps go
 // d-chunk by d-chunk, alternating the 32-key blocks (independent accumulators); the K operand
-// of step i + PF - 1 is read before the MFMA of step i.
-template <bool BF16, int D, int BC, int PF = 3>
+// of step i + PF - 1 is read before the MFMA of step i.  hook(i) runs at the start of step i
+// (used to slip other instructions, such as tile loads, between the MFMAs).
+struct NoHook {
+  template <class I> __device__ __forceinline__ void operator()(I) const {}
+};
+
+// Calls f(std::integral_constant<int, k>{}) for the k in [0, N) with i == k * STRIDE, if any.
+// Meant for an i that is a constant after loop unrolling: the tests then fold away.
+template <int N, int STRIDE, class F>
+__device__ __forceinline__ void at_step(int i, F&& f) {
+  static_for<N>([&](auto kc) XATTN_INLINE {
+    if (i == decltype(kc)::value * STRIDE) f(kc);
+  });
+}
+
+template <bool BF16, int D, int BC, int PF = 3, class Hook = NoHook>
 __device__ __forceinline__ void mma_scores(const char* kt, const LaneOffsets<D>& lo,
-                                           const i32x4 (&qf)[D / 16], f32x16 (&s)[BC / 32]) {
+                                           const i32x4 (&qf)[D / 16], f32x16 (&s)[BC / 32],
+                                           const Hook& hook = Hook()) {
   constexpr int KB = BC / 32, N = (D / 16) * KB;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  auto read = [&](int i) {
+  auto read = [&](int i) XATTN_INLINE {
     return *(const i32x4*)(kt + lo.kofs(i / KB, i % KB));
   };
   i32x4 buf[PF];
 #pragma unroll
   for (int i = 0; i < PF - 1; ++i) buf[i] = read(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
+  static_for<N>([&](auto ic) XATTN_INLINE {
+    constexpr int i = decltype(ic)::value;
+    hook(ic);
+    if constexpr (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
     sched_fence();
     s[i % KB] = Elt<BF16>::mfma(buf[i % PF], qf[i / KB], s[i % KB]);
     sched_fence();
-  }
+  });
 }
 
-// Set invisible scores to -inf: key k0 + (tile position) against query qrow.
+// Set invisible scores to -inf: key k0 + (tile position) against query qrow.  Register r of
+// block kb holds tile offset c = 32 kb + 8 (r / 4) + 4 hh + r % 4; the lane's visible offsets
+// form one range [lo, hi] (the key bounds of the row, clipped to the sequence), so each score
+// takes one clamp and one compare: c is visible iff clamp(c, lo, hi) == c.
 template <int BC>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[BC / 32], int k0, int qrow, int seqlen,
                                             int wl, int wr, int hh) {
+  const int base = k0 + 4 * hh;
+  int lo = wl >= 0 ? qrow - wl - base : -(1 << 30);
+  int hi = seqlen - 1 - base;
+  if (wr >= 0) hi = min(hi, qrow + wr - base);
+  if (lo > hi) lo = hi = -(1 << 30);  // nothing visible: no offset c >= 0 survives the clamp
 #pragma unroll
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const bool vis = key < seqlen && (wr < 0 || key <= qrow + wr) &&
-                       (wl < 0 || key >= qrow - wl);
-      if (!vis) s[kb][r] = -INFINITY;
+      const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+      if (min(max(c, lo), hi) != c) s[kb][r] = -INFINITY;
     }
 }
 
 // Online softmax of one tile (base 2) with a lazily moved reference max.  Turns the scores
 // into P packed to 16-bit (the B operand of O^T += V^T P^T), updates m and the lane's partial
 // l, and returns the factor O must be multiplied by (1 unless the reference max moved).
-// `moved` tells whether any row of the lane moved it.
-template <bool BF16, int BC>
+// `moved` tells whether any row of the lane moved it.  hook(i) runs before the exponential of
+// the lane's i-th score (used to spread other instructions, such as tile loads, over the step).
+template <bool BF16, int BC, class Hook = NoHook>
 __device__ __forceinline__ float softmax_tile(f32x16 (&s)[BC / 32], i32x4 (&pf)[BC / 16],
                                               float c2, float& m_run, float& l_run,
-                                              bool& moved) {
+                                              bool& moved, const Hook& hook = Hook()) {
   // Row max and row sum over the lane's BC / 2 scores use NP independent partial chains: the
   // serial chain of dependent max / add instructions is what bounds this step otherwise.
   constexpr int NP = 4;
@@ -372,6 +429,7 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[BC / 32], i32x4 (&pf)[
   for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      hook(kb * 16 + r);  // a constant once the loops are unrolled
       const float e = fast_exp2(fmaf(s[kb][r], c2, -m_use));
       s[kb][r] = e;
       ps[r % NP] += e;
@@ -403,12 +461,13 @@ __device__ __forceinline__ void scale_o(f32x16 (&o)[D / 32], float alpha) {
 // operand (V^T) for lane l is column d = 32 db + l % 32, keys 16 kc + 4 hh + {0..3} and
 // 16 kc + 8 + 4 hh + {0..3}: the key slots the S^T accumulator gave P.  Two transpose reads
 // fetch them.  Steps alternate the column blocks (independent accumulators); the operand of
-// step i + PF - 1 is read before the MFMA of step i.
-template <bool BF16, int D, int BC, int PF = 3>
+// step i + PF - 1 is read before the MFMA of step i; hook(i) runs at the start of step i.
+template <bool BF16, int D, int BC, int PF = 3, class Hook = NoHook>
 __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
-                                       const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32]) {
+                                       const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32],
+                                       const Hook& hook = Hook()) {
   constexpr int ROWB = D * 2, DB = D / 32, N = (BC / 16) * DB;
-  auto read = [&](int i) {
+  auto read = [&](int i) XATTN_INLINE {
     const char* p = vt + lo.vofs(i % DB, i / DB);
     const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
     const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p + 8 * ROWB));
@@ -417,13 +476,14 @@ __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
   i32x4 buf[PF];
 #pragma unroll
   for (int i = 0; i < PF - 1; ++i) buf[i] = read(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
+  static_for<N>([&](auto ic) XATTN_INLINE {
+    constexpr int i = decltype(ic)::value;
+    hook(ic);
+    if constexpr (i + PF - 1 < N) buf[(i + PF - 1) % PF] = read(i + PF - 1);
     sched_fence();
     o[i % DB] = Elt<BF16>::mfma(buf[i % PF], pf[i / DB], o[i % DB]);
     sched_fence();
-  }
+  });
 }
 
 // Epilogue for one 32-row block: O = O / l (16-bit, round to nearest even) and

@@ -12,12 +12,14 @@
 // kernels on page "flash_fwd_kernel.h" (@26a6e0a, the MMA warpgroups working while others do
 // softmax) realised with wave64 barriers instead of warpgroup specialisation.
 //
-// K and V tiles (64 keys) are loaded by group B during its softmax half, straight from global
-// memory into LDS (global_load_lds_dwordx4: lane l writes LDS base + 16 l, so the XOR swizzle
-// is applied by choosing which 16-byte chunk each lane fetches).  A tile has two half-phases
-// to arrive before it is read; buffers are double-buffered per matrix.  Rows past the end of
-// the sequence fetch the last valid row instead (finite data; those keys are masked to -inf,
-// so they contribute exactly 0).
+// K and V tiles (64 keys) are loaded by group B, straight from global memory into LDS
+// (buffer_load ... lds: lane l writes LDS base + 16 l, so the XOR swizzle is applied by choosing
+// which 16-byte chunk each lane fetches).  The load instructions are spread thinly over B's
+// softmax step: a wave that issues several of them back to back stalls until the address unit
+// has taken the others.  They target the buffer nobody reads in that half-phase and have two
+// half-phases to arrive.  Buffers are double-buffered per matrix.  Rows past the end of the
+// sequence fetch the last valid row instead (finite data; those keys are masked to -inf, so
+// they contribute exactly 0).
 //
 // Half-phase schedule (h counts barriers; U_u = {V_u, K_{u+1}} lives in buffer u & 1):
 //   h = 2j   : A softmax(j)              | B  O += V_{j-1} P_{j-1}, S_j = K_j Q^T
@@ -100,7 +102,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
   // p holds row p / CH, chunk (p % CH) ^ swizzle(row); since LOADERS * 64 / CH rows is a whole
   // number of swizzle periods, instruction i reads the bytes of instruction 0 shifted by
   // i * 4096, so one per-lane offset serves all of them (the shift goes to the scalar offset).
-  const int lw = wave - 4;  // loader index within group B
+  const int lw = __builtin_amdgcn_readfirstlane(wave & 3);  // loader index within group B
   static_assert((LOADERS * 64 / CH) % 16 == 0, "loader rows must cover whole swizzle periods");
   const int lrow = (lw * 64 + lane) / CH;  // row of this lane's slot in instruction 0
   const int lch = (lw * 64 + lane) % CH;
@@ -109,68 +111,116 @@ void attn_fwd_pp_kernel(FwdArgs a) {
   const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * D * 2);
   const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * D * 2);
   constexpr int ISTEP = LOADERS * 64 * 16;  // bytes per load instruction (all loader waves)
-  auto load_tile = [&](const i32x4& rsrc, int voff0, int swz_shift_k, int r, char* dst) {
+  // instruction II of the load of K (is_k) or V tile r into the LDS buffer at `dst`
+  auto load_one = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
+    constexpr bool is_k = decltype(k_tile)::value;
+    constexpr int II = decltype(ii)::value;
     const int kbase = (t_lo + r) * BC;
+    const unsigned lds = dst + lw * 1024;
     if (kbase + BC <= seqlen) {
-#pragma unroll
-      for (int i = 0; i < LI; ++i)
-        buffer_load_lds16(rsrc, voff0, kbase * D * 2 + i * ISTEP, dst + i * ISTEP + lw * 1024);
+      buffer_load_lds16_at<II * ISTEP, II * ISTEP>(is_k ? rsrc_k : rsrc_v, is_k ? voff_k : voff_v,
+                                                   kbase * D * 2, lds);
     } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
-#pragma unroll
-      for (int i = 0; i < LI; ++i) {
-        const int row = lrow + i * (LOADERS * 64 / CH);
-        const int crow = min(row, seqlen - 1 - kbase);
-        const int sw = swz_shift_k ? swz_k<D>(row) : swz_v<D>(row);
-        buffer_load_lds16(rsrc, crow * D * 2 + ((lch ^ sw) << 4), kbase * D * 2,
-                          dst + i * ISTEP + lw * 1024);
-      }
+      const int row = lrow + II * (LOADERS * 64 / CH);
+      const int crow = min(row, seqlen - 1 - kbase);
+      const int sw = is_k ? swz_k<D>(row) : swz_v<D>(row);
+      buffer_load_lds16_at<II * ISTEP, 0>(is_k ? rsrc_k : rsrc_v,
+                                          crow * D * 2 + ((lch ^ sw) << 4), kbase * D * 2, lds);
     }
   };
-  auto load_k = [&](int r, char* dst) { load_tile(rsrc_k, voff_k, 1, r, dst); };
-  auto load_v = [&](int r, char* dst) { load_tile(rsrc_v, voff_v, 0, r, dst); };
+  // instruction II of the load of a tile that lies wholly inside the sequence
+  auto load_full = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
+    constexpr bool is_k = decltype(k_tile)::value;
+    constexpr int II = decltype(ii)::value;
+    buffer_load_lds16_at<II * ISTEP, II * ISTEP>(is_k ? rsrc_k : rsrc_v, is_k ? voff_k : voff_v,
+                                                 (t_lo + r) * BC * D * 2, dst + lw * 1024);
+  };
+  auto load_all = [&](auto k_tile, int r, unsigned dst) XATTN_INLINE {
+    static_for<LI>([&](auto ii) XATTN_INLINE { load_one(k_tile, r, dst, ii); });
+  };
+  const std::true_type K_TILE;
+  const std::false_type V_TILE;
+  const unsigned k_lds0a = lds_address(k_lds0), k_lds1a = lds_address(k_lds1);
+  const unsigned v_lds0a = lds_address(v_lds0), v_lds1a = lds_address(v_lds1);
 
   // ---- the three per-tile steps of a wave (r = tile index relative to t_lo) ---------------
-  auto sees = [&](int r) {
+  auto sees = [&](int r) XATTN_INLINE {
     const int k0 = (t_lo + r) * BC;
     return wave_active && k0 <= kw_hi && k0 + BC - 1 >= kw_lo;
   };
-  auto step_scores = [&](int r, const char* kt) {
+  auto step_scores = [&](int r, const char* kt) XATTN_INLINE {
     if (sees(r)) mma_scores<BF16, D, BC, PF>(kt, lo, qf, sacc);
   };
-  auto step_softmax = [&](int r) {
-    if (!sees(r)) return;
+  // softmax of tile r; group B also issues the loads of U_{r+1} = {V_{r+1}, K_{r+2}}, one
+  // instruction every SL exponentials (all at once when the tile is not visible to the wave)
+  constexpr int NLD = 2 * LI, SL = (BC / 2) / NLD;
+  // (the d = 128 sliding-window variant runs out of registers with the second softmax copy)
+  constexpr bool SPREAD_LOADS = !(MODE == MASK_WINDOW && D > 64);
+  static_assert((BC / 2) % NLD == 0, "loads must spread evenly over the softmax");
+  auto step_softmax = [&](int r, bool ld_v, bool ld_k, unsigned vdst, unsigned kdst) XATTN_INLINE {
+    // spread the loads only in the common case (both tiles wanted and whole); otherwise issue
+    // them up front
+    const bool spread = SPREAD_LOADS && ld_v && ld_k && (t_lo + r + 3) * BC <= seqlen;
+    if (!spread) {
+      if (ld_v) load_all(V_TILE, r + 1, vdst);
+      if (ld_k) load_all(K_TILE, r + 2, kdst);
+    }
+    if (!sees(r)) {
+      if (spread) {
+        load_all(V_TILE, r + 1, vdst);
+        load_all(K_TILE, r + 2, kdst);
+      }
+      return;
+    }
     const int k0 = (t_lo + r) * BC;
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
     bool moved;
-    const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
+    float alpha;
+    if (spread) {  // one load instruction every SL exponentials: V first, then K
+      alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved, [&](int i) XATTN_INLINE {
+        at_step<NLD, SL>(i, [&](auto l) XATTN_INLINE {
+          constexpr int L = decltype(l)::value;
+          sched_fence();  // keep the loads where they are placed
+          if constexpr (L < LI)
+            load_full(V_TILE, r + 1, vdst, std::integral_constant<int, L>{});
+          else
+            load_full(K_TILE, r + 2, kdst, std::integral_constant<int, L - LI>{});
+          sched_fence();
+        });
+      });
+    } else {
+      alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
+    }
     if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
   };
-  auto step_pv = [&](int r, const char* vt) {
+  auto step_pv = [&](int r, const char* vt) XATTN_INLINE {
     if (sees(r)) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
   };
 
   // ---- prologue: K_0 (buffer 1), V_0 and K_1 (buffer 0) ---------------------------------
   if (!grp_a) {
-    load_k(0, k_lds1);
-    load_v(0, v_lds0);
-    if (n > 1) load_k(1, k_lds0);
+    load_all(K_TILE, 0, k_lds1a);
+    load_all(V_TILE, 0, v_lds0a);
+    if (n > 1) load_all(K_TILE, 1, k_lds0a);
     wait_vmem();
   }
   block_barrier();
   if (grp_a) step_scores(0, k_lds1);
 
   // ---- main loop: two half-phases per tile, buffer parity P = j & 1 known at compile time ----
-  auto iteration = [&](int j, auto parity) {
+  auto iteration = [&](int j, auto parity) XATTN_INLINE {
     constexpr int P = decltype(parity)::value;
     char* const kP = P ? k_lds1 : k_lds0;  // holds K_{j+1}
     char* const kQ = P ? k_lds0 : k_lds1;  // holds K_j, then receives K_{j+2}
     char* const vP = P ? v_lds1 : v_lds0;  // holds V_j
     char* const vQ = P ? v_lds0 : v_lds1;  // holds V_{j-1}, then receives V_{j+1}
+    const unsigned kQa = P ? k_lds0a : k_lds1a;
+    const unsigned vQa = P ? v_lds0a : v_lds1a;
     // half-phase 2j
     if (grp_a) {
-      if (j < n) step_softmax(j);
+      if (j < n) step_softmax(j, false, false, 0, 0);
     } else {
       __builtin_amdgcn_s_setprio(2);  // MFMA block: win issue over the partner's softmax
       if (j >= 1) step_pv(j - 1, vQ);
@@ -180,10 +230,6 @@ void attn_fwd_pp_kernel(FwdArgs a) {
     if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
     block_barrier();
     // half-phase 2j+1
-    if (!grp_a && j + 1 < n) {
-      if (j + 2 < n) load_k(j + 2, kQ);
-      load_v(j + 1, vQ);
-    }
     if (grp_a) {
       __builtin_amdgcn_s_setprio(2);
       if (j < n) {
@@ -192,7 +238,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
-      if (j < n) step_softmax(j);
+      if (j < n) step_softmax(j, j + 1 < n, j + 2 < n, vQa, kQa);
     }
     block_barrier();
   };
