@@ -81,10 +81,12 @@ def workload_bytes(w, cu=None) -> float:
 
 def kernel_name(w, cu=None) -> str:
     """The kernel the library launches for a workload (mirrors the host dispatch: the wide
-    kernel for d >= 256; for d <= 128 the ping-pong kernel once the grid of 256-row tiles has
-    at least 1024 workgroups, else the generic one)."""
+    kernel for d >= 256, the generic kernel for d = 64, and for d = 128 the ping-pong kernel
+    once the grid of 256-row tiles has at least 1024 workgroups, else the generic one)."""
     if w.head_dim >= 256:
         return "attn_fwd_wide_kernel"
+    if w.head_dim == 64:
+        return "attn_fwd_kernel"
     if w.varlen:
         tiles = w.heads * ((int(cu[-1]) + 255) // 256)
     else:

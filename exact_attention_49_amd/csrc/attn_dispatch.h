@@ -25,8 +25,10 @@ template <class T> struct UseGeneric {
 
 template <int D> struct TileCfg;
 template <> struct TileCfg<64> {
-  using Big = UsePingPong;
-  using Small = UseGeneric<Tile<4, 64, 2, 3>>;
+  // at d = 64 the softmax outweighs the MFMA work, and three independent waves per SIMD
+  // interleave it better than the two-group ping-pong
+  using Big = UseGeneric<Tile<4, 64, 2, 3>>;
+  using Small = Big;
 };
 template <> struct TileCfg<128> {
   using Big = UsePingPong;

@@ -1,4 +1,5 @@
-// Ping-pong exact-attention forward kernel for gfx950 (head dims 64 and 128).
+// Ping-pong exact-attention forward kernel for gfx950 (head dim 128; the shape also compiles
+// for 64, where the generic kernel is faster).
 //
 // A workgroup is 8 waves of 32 query rows (256 rows of one (batch|sequence, head)); the waves
 // are split into two groups of four, A (waves 0-3) and B (waves 4-7), so that each SIMD runs

@@ -15,6 +15,8 @@
 // for after it, with one barrier per tile.  The math per tile is in attn_common.h.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace xattn {
@@ -81,6 +83,44 @@ __device__ __forceinline__ void mma_pv_agpr(const char* vt, const LaneOffsets<D>
     mfma_agpr<BF16>(o[i % DB], buf[i % PF], pf[i / DB]);
     sched_fence();
   }
+}
+
+// Epilogue of one wave's 32 rows: O / l rounded to 16-bit, staged in this wave's LDS region
+// (32 rows x 2D bytes, 16-byte chunk c of row r at chunk position c ^ r) and read back row by
+// row, so that every global store instruction writes whole rows.  Rows past the end of the
+// sequence are not stored.  LSE = (m + log2 l) ln 2.  Called by all lanes of the wave; the
+// region must not be in use by any other wave.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, int qw0, int seqlen,
+                                                  int lane, const f32x16 (&o)[D / 32],
+                                                  float m_run, float l_run, char* region) {
+  constexpr float LN2 = 0.693147180559945309f;
+  constexpr int ROWB = D * 2, CH = D / 8, RPI = 64 / CH;  // rows per 64-lane read
+  static_assert(CH <= 64 && 64 % CH == 0 && CH >= 32, "one row spans 32 or 64 chunks");
+  const int l32 = lane & 31, hh = lane >> 5;
+  const float lt = halves_sum(l_run);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& x = o[db];
+      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
+                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
+      const int c = 4 * db + g4;  // 16-byte chunk of d = 32 db + 8 g4 .. + 7; this lane's half hh
+      *(i32x2*)(region + l32 * ROWB + ((c ^ l32) << 4) + hh * 8) = val;
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  const int rsub = lane / CH, c = lane % CH;
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + rsub;
+    const i32x4 v = *(const i32x4*)(region + r * ROWB + ((c ^ r) << 4));
+    if (qw0 + r < seqlen) *(i32x4*)(a.o + (row0 + qw0 + r) * D + c * 8) = v;
+  }
+  const int qrow = qw0 + l32;
+  if (a.lse != nullptr && hh == 0 && qrow < seqlen)
+    a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
 template <bool BF16, int D, int MODE>
@@ -183,11 +223,47 @@ void attn_fwd_wide_kernel(FwdArgs a) {
     }
   };
 
-  auto consume = [&](int t, const char* kt, const char* vt) {
+  // instruction II of the K (or V) load of a tile that lies wholly inside the sequence
+  const unsigned wave_lds = wave * 1024;
+  auto load_full = [&](auto k_tile, int t, unsigned dst, auto ii) XATTN_INLINE {
+    constexpr int II = decltype(ii)::value;
+    if constexpr (decltype(k_tile)::value)
+      buffer_load_lds16_at<II * 4 * 1024, (II / NKO) * NKO * R * ROWB>(
+          rsrc_k, koff[II % NKO], t * BC * ROWB, dst + wave_lds);
+    else
+      buffer_load_lds16_at<II * 4 * 1024, (II / NVO) * NVO * R * ROWB>(
+          rsrc_v, voff[II % NVO], t * BC * ROWB, dst + wave_lds);
+  };
+
+  // One K/V tile: S^T, mask, online softmax, O^T update.  With ld, the loads of tile t + 1
+  // (into kdst / vdst) are slipped between the score MFMAs, one instruction every SH of them;
+  // a partial next tile or a tile this wave does not see gets them all up front.
+  constexpr int NS = (D / 16) * (BC / 32), SH = NS / (2 * LI);
+  static_assert(NS % (2 * LI) == 0, "loads must spread evenly over the score MFMAs");
+  auto consume = [&](int t, const char* kt, const char* vt, bool ld, unsigned kdst,
+                     unsigned vdst) XATTN_INLINE {
     const int k0 = t * BC;
-    if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;  // nothing visible
+    const bool vis = wave_active && k0 <= kw_hi && k0 + BC - 1 >= kw_lo;
+    const bool spread = ld && vis && (t + 2) * BC <= seqlen;
+    if (ld && !spread) load_tile(t + 1, kdst, vdst);
+    if (!vis) return;  // nothing visible
     f32x16 sacc[BC / 32];
-    mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
+    if (spread) {
+      mma_scores<BF16, D, BC>(kt, lo, qf, sacc, [&](auto i) XATTN_INLINE {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I % SH == 0) {
+          constexpr int L = I / SH;  // K instructions first, then V
+          sched_fence();
+          if constexpr (L < LI)
+            load_full(std::true_type{}, t + 1, kdst, std::integral_constant<int, L>{});
+          else
+            load_full(std::false_type{}, t + 1, vdst, std::integral_constant<int, L - LI>{});
+          sched_fence();
+        }
+      });
+    } else {
+      mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
+    }
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
@@ -209,19 +285,20 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   wait_vmem();
   block_barrier();
   for (int t = t_lo; t <= t_hi; t += 2) {
-    if (t + 1 <= t_hi) load_tile(t + 1, k1a, v1a);
-    consume(t, k_lds0, v_lds0);
+    consume(t, k_lds0, v_lds0, t + 1 <= t_hi, k1a, v1a);
     wait_vmem();
     block_barrier();
     if (t + 1 > t_hi) break;
-    if (t + 2 <= t_hi) load_tile(t + 2, k0a, v0a);
-    consume(t + 1, k_lds1, v_lds1);
+    consume(t + 1, k_lds1, v_lds1, t + 2 <= t_hi, k0a, v0a);
     wait_vmem();
     block_barrier();
   }
 
+  // all waves are past the last barrier: the tile buffers are free, one per wave
   agpr_settle(oacc);
-  if (wave_active) store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  char* const region = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+  static_assert(TILEB == 32 * ROWB, "a tile buffer holds one wave's 32 output rows");
+  if (wave_active) store_rows_staged<BF16, D>(a, w.row0, qw0, seqlen, lane, oacc, m_run, l_run, region);
 }
 
 }  // namespace xattn
