@@ -12,8 +12,10 @@ steps between two device synchronisations.  Rank 0 prints one JSON line:
            per-launch durations measured with HIP events on the launch stream
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
 
-Other flags: --flush touches 512 MiB between steps (cache-cold timing), --list-workloads,
---calibrate-copy runs only a plain device copy of known size (for scaling HBM counters).
+Besides the warm timing, a short second pass times the same launches with 512 MiB of other
+device traffic between them (reported as cold_cache; --no-cold skips it).  Other flags:
+--flush makes the main timing cache-cold too, --list-workloads, --calibrate-copy runs only a
+plain device copy of known size (for scaling HBM counters).
 """
 
 from __future__ import annotations
@@ -161,9 +163,16 @@ def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
         sample = (f"{len(units)} of {w.batch * w.heads} (batch, head) pairs, whole "
                   f"(N={w.seqlen}, d={w.head_dim}), fp64 numpy")
     del np
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": sample, "seconds": round(t_total, 2),
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -187,6 +196,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--flush", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the extra cache-cold timing pass reported beside the warm one")
     ap.add_argument("--list-workloads", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -239,21 +250,38 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(1)
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    def timed(steps, flush):
+        """Launch `steps` steps; returns (wall seconds, per-launch ms from HIP events)."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush.fill_(1)
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    wall, launch_ms = timed(args.steps, flush_buf)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
+    srt = sorted(launch_ms)
+    med_launch_ms, min_launch_ms = srt[len(srt) // 2], srt[0]
+    # the same launches with 512 MiB of other traffic between them (cold caches), for context
+    cold = None
+    if not args.no_cold:
+        cold_buf = flush_buf if flush_buf is not None else torch.empty(
+            512 << 20, dtype=torch.uint8, device=dev)
+        _, cold_ms = timed(min(args.steps, 20), cold_buf)
+        cold_avg = sum(cold_ms) / len(cold_ms)
+        cold = {"avg_launch_ms": round(cold_avg, 4),
+                "tflops": round(workload_flops(w, cu) / (cold_avg / 1e3) / 1e12, 2),
+                "launches": len(cold_ms), "between_launches": "512 MiB device fill"}
+        del cold_buf
 
     flops = workload_flops(w, cu)
     algo_bytes = workload_bytes(w, cu)
@@ -266,8 +294,11 @@ def main() -> int:
               "causal": w.causal, "window_left": w.window_left,
               "window_right": w.window_right, "seed": w.seed, "value_scale": w.value_scale}
     if w.varlen:
-        config.update(num_seqs=w.num_seqs, total_tokens=int(cu[-1]),
-                      lengths=(cu[1:] - cu[:-1]).tolist())
+        lens = (cu[1:] - cu[:-1]).tolist()
+        config.update(num_seqs=w.num_seqs, total_tokens=int(cu[-1]), lengths=lens,
+                      flops_counted="4*H*d*(visible pairs)",
+                      flops_formula_literal=sum(2.0 * w.heads * n * n * w.head_dim
+                                                for n in lens))
     else:
         config.update(batch=w.batch, seqlen=w.seqlen)
     out = {
@@ -282,10 +313,14 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel": kernel_name(w, cu),
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "median_launch_ms": round(med_launch_ms, 4),
+                     "min_launch_ms": round(min_launch_ms, 4),
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_budget)
         out["cpu_baseline"]["speedup_gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
