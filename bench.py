@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = one forward pass (one attn_fwd / attn_fwd_varlen launch) over the workload's
+One step = one forward pass (one attn_fwd / attn_fwd_varlen call; for the split-KV workload
+one attn_fwd_splitkv call, which runs the split sweep and the merge) over the workload's
 inputs, which are resident in HBM before timing starts.  W untimed steps, then exactly K timed
 steps between two device synchronisations.  Rank 0 prints one JSON line:
 
@@ -85,6 +86,9 @@ def kernel_name(w, cu=None) -> str:
     """The kernel the library launches for a workload (mirrors the host dispatch: the wide
     kernel for d >= 256, the generic kernel for d = 64, and for d = 128 the ping-pong kernel
     once the grid of 256-row tiles has at least 1024 workgroups, else the generic one)."""
+    if w.splitkv:  # one step = the split sweep and the merge
+        base = "attn_fwd_wide_kernel" if w.head_dim >= 256 else "attn_fwd_kernel"
+        return f"{base} (split-KV) + attn_merge_kernel"
     if w.head_dim >= 256:
         return "attn_fwd_wide_kernel"
     if w.head_dim == 64:
@@ -218,7 +222,8 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_49_amd import attn_fwd, attn_fwd_varlen
+    from exact_attention_49_amd import (attn_fwd, attn_fwd_splitkv, attn_fwd_varlen,
+                                        splitkv_num_splits, splitkv_workspace_size)
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     cu = None
@@ -234,8 +239,17 @@ def main() -> int:
     cud = cu.to(dev) if cu is not None else None
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
 
+    ws = None
+    if w.splitkv:  # caller-owned workspace, allocated before any timing
+        nbytes = splitkv_workspace_size(w.batch, w.heads, w.seqlen, w.head_dim, 0)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
     def step():
-        if w.varlen:
+        if w.splitkv:
+            attn_fwd_splitkv(qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                             window_right=w.window_right, out=od, lse=lsed, num_splits=0,
+                             workspace=ws)
+        elif w.varlen:
             attn_fwd_varlen(qd, kd, vd, cud, max_len, causal=w.causal,
                             window_left=w.window_left, window_right=w.window_right, out=od,
                             lse=lsed)
@@ -301,6 +315,9 @@ def main() -> int:
                                                 for n in lens))
     else:
         config.update(batch=w.batch, seqlen=w.seqlen)
+    if w.splitkv:
+        config.update(entry_point="attn_fwd_splitkv",
+                      num_splits=splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim))
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -321,6 +338,21 @@ def main() -> int:
     }
     if cold is not None:
         out["cold_cache"] = cold
+    if w.splitkv:  # the same problem through the plain entry point, for context
+        def plain():
+            attn_fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                     window_right=w.window_right, out=od, lse=lsed)
+        for _ in range(3):
+            plain()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(20):
+            plain()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        pm = ev0.elapsed_time(ev1) / 20
+        out["plain_path"] = {"entry_point": "attn_fwd", "avg_launch_ms": round(pm, 4),
+                             "tflops": round(flops / (pm / 1e3) / 1e12, 2)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_budget)
         out["cpu_baseline"]["speedup_gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)

@@ -14,8 +14,10 @@ import threading
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "library_path", "load_library",
-           "STATUS", "EXPORTED_SYMBOLS"]
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv",
+           "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
+           "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "library_path",
+           "load_library", "STATUS", "EXPORTED_SYMBOLS"]
 
 LIB_NAME = "libexact_attn.so"
 
@@ -32,11 +34,19 @@ STATUS = {
 }
 
 # (name, restype, argtypes) for every function include/exact_attn.h declares
-_P, _I, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 EXPORTED_SYMBOLS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P]),
+    "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P,
+                              _S, _P]),
+    "attn_fwd_varlen_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                     _I, _I, _I, _P, _S, _P]),
+    "attn_fwd_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
+    "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
+    "attn_fwd_varlen_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -94,14 +104,7 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-             window_left: int = -1, window_right: int = -1,
-             softmax_scale: float | None = None, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None, return_lse: bool = True):
-    """Dense attention forward.  q, k, v: [B, H, N, d] fp16/bf16 on one GPU.
-
-    Returns (o, lse) with o like q and lse fp32 [B, H, N] (lse is None if return_lse is False
-    and no lse buffer was given).  Launches on the current stream."""
+def _dense_args(q, k, v, softmax_scale, out, lse, return_lse):
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _device_tensor(t, n)
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -122,23 +125,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
         _device_tensor(lse, "lse")
         if lse.shape != (bsz, nh, n) or lse.dtype != torch.float32:
             raise AttnError("lse must be float32 [B, H, N]")
-    lib = load_library()
-    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                      lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
-                      DTYPE_CODES[q.dtype], float(softmax_scale), int(bool(causal)),
-                      int(window_left), int(window_right), _stream_handle(q.device))
-    _check(st, "attn_fwd")
-    return out, lse
+    return bsz, nh, n, d, float(softmax_scale), out, lse
 
 
-def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                    cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
-                    window_left: int = -1, window_right: int = -1,
-                    softmax_scale: float | None = None, out: torch.Tensor | None = None,
-                    lse: torch.Tensor | None = None, return_lse: bool = True):
-    """Packed variable-length forward.  q, k, v: [H, total, d]; cu_seqlens: int32 GPU tensor
-    [num_seqs + 1]; max_seqlen: a host bound on the sequence lengths.
-    Returns (o [H, total, d], lse fp32 [H, total])."""
+def _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse, return_lse):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens")):
         _device_tensor(t, n)
     if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
@@ -161,12 +151,128 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _device_tensor(lse, "lse")
         if lse.shape != (nh, total) or lse.dtype != torch.float32:
             raise AttnError("lse must be float32 [H, total_tokens]")
+    return nh, total, d, float(softmax_scale), out, lse
+
+
+def _workspace(nbytes: int, workspace, device):
+    """A device workspace of at least nbytes (allocated here, by torch, when none is given)."""
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _device_tensor(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise AttnError(f"workspace must hold at least {nbytes} bytes")
+    return workspace
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             window_left: int = -1, window_right: int = -1,
+             softmax_scale: float | None = None, out: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Dense attention forward.  q, k, v: [B, H, N, d] fp16/bf16 on one GPU.
+
+    Returns (o, lse) with o like q and lse fp32 [B, H, N] (lse is None if return_lse is False
+    and no lse buffer was given).  Launches on the current stream."""
+    bsz, nh, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse, return_lse)
+    lib = load_library()
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
+                      DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                      int(window_left), int(window_right), _stream_handle(q.device))
+    _check(st, "attn_fwd")
+    return out, lse
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                    window_left: int = -1, window_right: int = -1,
+                    softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Packed variable-length forward.  q, k, v: [H, total, d]; cu_seqlens: int32 GPU tensor
+    [num_seqs + 1]; max_seqlen: a host bound on the sequence lengths.
+    Returns (o [H, total, d], lse fp32 [H, total])."""
+    nh, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse,
+                                                 return_lse)
     lib = load_library()
     st = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
                              cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen),
-                             total, nh, d, DTYPE_CODES[q.dtype], float(softmax_scale),
+                             total, nh, d, DTYPE_CODES[q.dtype], scale,
                              int(bool(causal)), int(window_left), int(window_right),
                              _stream_handle(q.device))
     _check(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def splitkv_num_splits(batch: int, heads: int, seqlen: int, head_dim: int) -> int:
+    """The split count the library picks for num_splits = 0 (1 = no split)."""
+    return load_library().attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim)
+
+
+def splitkv_workspace_size(batch: int, heads: int, seqlen: int, head_dim: int,
+                           num_splits: int = 0) -> int:
+    """Workspace bytes attn_fwd_splitkv needs (0: none)."""
+    return load_library().attn_fwd_splitkv_workspace_size(batch, heads, seqlen, head_dim,
+                                                          num_splits)
+
+
+def varlen_splitkv_num_splits(num_seqs: int, max_seqlen: int, total_tokens: int, heads: int,
+                              head_dim: int) -> int:
+    return load_library().attn_fwd_varlen_splitkv_num_splits(num_seqs, max_seqlen,
+                                                             total_tokens, heads, head_dim)
+
+
+def varlen_splitkv_workspace_size(num_seqs: int, max_seqlen: int, total_tokens: int,
+                                  heads: int, head_dim: int, num_splits: int = 0) -> int:
+    return load_library().attn_fwd_varlen_splitkv_workspace_size(
+        num_seqs, max_seqlen, total_tokens, heads, head_dim, num_splits)
+
+
+def attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     window_left: int = -1, window_right: int = -1,
+                     softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None, return_lse: bool = True,
+                     num_splits: int = 0, workspace: torch.Tensor | None = None):
+    """attn_fwd with the key range of every q-tile split over num_splits work items (0: the
+    library chooses) and merged.  The workspace is allocated here unless one is given."""
+    bsz, nh, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse, return_lse)
+    lib = load_library()
+    nbytes = lib.attn_fwd_splitkv_workspace_size(bsz, nh, n, d, int(num_splits))
+    ws = _workspace(nbytes, workspace, q.device)
+    st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
+                              DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                              int(window_left), int(window_right), int(num_splits),
+                              ws.data_ptr() if ws is not None else None,
+                              ws.numel() * ws.element_size() if ws is not None else 0,
+                              _stream_handle(q.device))
+    _check(st, "attn_fwd_splitkv")
+    return out, lse
+
+
+def attn_fwd_varlen_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                            window_left: int = -1, window_right: int = -1,
+                            softmax_scale: float | None = None,
+                            out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                            return_lse: bool = True, num_splits: int = 0,
+                            workspace: torch.Tensor | None = None):
+    """attn_fwd_varlen with split-KV (see attn_fwd_splitkv)."""
+    nh, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse,
+                                                 return_lse)
+    lib = load_library()
+    ns = cu_seqlens.numel() - 1
+    nbytes = lib.attn_fwd_varlen_splitkv_workspace_size(ns, int(max_seqlen), total, nh, d,
+                                                        int(num_splits))
+    ws = _workspace(nbytes, workspace, q.device)
+    st = lib.attn_fwd_varlen_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     cu_seqlens.data_ptr(), ns, int(max_seqlen), total, nh, d,
+                                     DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                                     int(window_left), int(window_right), int(num_splits),
+                                     ws.data_ptr() if ws is not None else None,
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
+                                     _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen_splitkv")
     return out, lse

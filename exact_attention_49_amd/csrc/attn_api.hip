@@ -13,6 +13,14 @@ template <> hipError_t launch_fwd<64>(const FwdArgs&, bool, int, bool, int, hipS
 template <> hipError_t launch_fwd<128>(const FwdArgs&, bool, int, bool, int, hipStream_t);
 template <> hipError_t launch_fwd<256>(const FwdArgs&, bool, int, bool, int, hipStream_t);
 template <> hipError_t launch_fwd<512>(const FwdArgs&, bool, int, bool, int, hipStream_t);
+template <> hipError_t launch_fwd_split<64>(const FwdArgs&, bool, int, int, hipStream_t);
+template <> hipError_t launch_fwd_split<128>(const FwdArgs&, bool, int, int, hipStream_t);
+template <> hipError_t launch_fwd_split<256>(const FwdArgs&, bool, int, int, hipStream_t);
+template <> hipError_t launch_fwd_split<512>(const FwdArgs&, bool, int, int, hipStream_t);
+template <> hipError_t launch_merge<64>(const MergeArgs&, bool, hipStream_t);
+template <> hipError_t launch_merge<128>(const MergeArgs&, bool, hipStream_t);
+template <> hipError_t launch_merge<256>(const MergeArgs&, bool, hipStream_t);
+template <> hipError_t launch_merge<512>(const MergeArgs&, bool, hipStream_t);
 }  // namespace xattn
 
 namespace {
@@ -59,56 +67,104 @@ int mask_mode(int causal, int max_len, int* wl, int* wr) {
   return xattn::MASK_WINDOW;
 }
 
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_ERR_HIP;
+}
+
 int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big, long n_work,
            void* stream) {
   if (n_work <= 0) return ATTN_OK;
   if (n_work > std::numeric_limits<int>::max()) return ATTN_ERR_TOO_LARGE;
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (head_dim) {
+    case 64: return hip_status(xattn::launch_fwd<64>(a, bf16, mode, big, (int)n_work, s));
+    case 128: return hip_status(xattn::launch_fwd<128>(a, bf16, mode, big, (int)n_work, s));
+    case 256: return hip_status(xattn::launch_fwd<256>(a, bf16, mode, big, (int)n_work, s));
+    default: return hip_status(xattn::launch_fwd<512>(a, bf16, mode, big, (int)n_work, s));
+  }
+}
+
+// Split-KV: the split sweep (grid = n_work x num_splits) and then the merge.
+int launch_split(int head_dim, const xattn::FwdArgs& a, const xattn::MergeArgs& m, int dtype,
+                 int mode, long n_work, void* stream) {
+  const long grid = n_work * a.num_splits;
+  if (n_work <= 0) return ATTN_OK;
+  if (grid > std::numeric_limits<int>::max() || (m.rows + 3) / 4 > 0x7fffffffL)
+    return ATTN_ERR_TOO_LARGE;
+  const bool bf16 = dtype == ATTN_DTYPE_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   switch (head_dim) {
-    case 64: e = xattn::launch_fwd<64>(a, bf16, mode, big, (int)n_work, s); break;
-    case 128: e = xattn::launch_fwd<128>(a, bf16, mode, big, (int)n_work, s); break;
-    case 256: e = xattn::launch_fwd<256>(a, bf16, mode, big, (int)n_work, s); break;
-    default: e = xattn::launch_fwd<512>(a, bf16, mode, big, (int)n_work, s); break;
+    case 64: e = xattn::launch_fwd_split<64>(a, bf16, mode, (int)grid, s); break;
+    case 128: e = xattn::launch_fwd_split<128>(a, bf16, mode, (int)grid, s); break;
+    case 256: e = xattn::launch_fwd_split<256>(a, bf16, mode, (int)grid, s); break;
+    default: e = xattn::launch_fwd_split<512>(a, bf16, mode, (int)grid, s); break;
   }
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return ATTN_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
+  switch (head_dim) {
+    case 64: return hip_status(xattn::launch_merge<64>(m, bf16, s));
+    case 128: return hip_status(xattn::launch_merge<128>(m, bf16, s));
+    case 256: return hip_status(xattn::launch_merge<256>(m, bf16, s));
+    default: return hip_status(xattn::launch_merge<512>(m, bf16, s));
   }
-  return ATTN_OK;
 }
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr long kMaxRows = 1L << 40;  // rows * head_dim stays far inside int64
 // The kernels address one sequence's K/V rows with 32-bit byte offsets (buffer loads).
 constexpr long kMaxSeqBytes = (1L << 31) - 1;
+constexpr int kMaxSplits = 64;
+// MI355X: 256 compute units.  Workgroups of the small shape resident per CU at once: three at
+// d = 64, two at d = 128 (register-bound), one for the wide head dims (LDS-bound).
+constexpr int kNumCUs = 256;
+int resident_per_cu(int d) { return d == 64 ? 3 : d == 128 ? 2 : 1; }
+// Keys per K/V tile of the small shape.
+int small_tile_keys(int d) { return d >= 256 ? xattn::WideShape::BC : 64; }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-             int heads, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
-             int window_left, int window_right, void* stream) {
-  if (batch < 0 || heads < 0 || seqlen < 0) return ATTN_ERR_INVALID_ARG;
-  const long rows = (long)batch * heads * seqlen;
-  if (rows == 0) {  // empty problem: still reject malformed non-size arguments
-    if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
-    return ATTN_OK;
-  }
-  int st = check_common(q, k, v, o, lse, head_dim, dtype, softmax_scale, causal, window_left,
-                        window_right);
-  if (st != ATTN_OK) return st;
-  if (rows > kMaxRows) return ATTN_ERR_TOO_LARGE;
-  if ((long)seqlen * head_dim * 2 > kMaxSeqBytes) return ATTN_ERR_TOO_LARGE;
-  int wl = window_left, wr = window_right;
-  const int mode = mask_mode(causal, seqlen, &wl, &wr);
-  const bool big = (long)batch * heads * ((seqlen + block_rows(head_dim, true) - 1) /
-                                          block_rows(head_dim, true)) >= xattn::BIG_TILE_MIN_WORK;
-  const int br = block_rows(head_dim, big);
+// A validated launch: the kernel arguments and the grid for one tile shape.
+struct Plan {
+  int status = ATTN_OK;
+  bool empty = false;    // nothing to compute (a zero size): return OK without launching
   xattn::FwdArgs a{};
+  int mode = 0;
+  bool big = false;
+  long n_work = 0;       // workgroups of one sweep (one split)
+  long rows = 0;         // rows of o
+  int max_len = 0;       // longest sequence
+};
+
+// shape: 1 = choose (big if the grid is large enough), 0 = small shape.
+Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                int heads, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
+                int window_left, int window_right, int shape) {
+  Plan p;
+  if (batch < 0 || heads < 0 || seqlen < 0) { p.status = ATTN_ERR_INVALID_ARG; return p; }
+  p.rows = (long)batch * heads * seqlen;
+  if (p.rows == 0) {  // empty problem: still reject malformed non-size arguments
+    if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16)
+      p.status = ATTN_ERR_UNSUPPORTED_DTYPE;
+    else if (!supported_head_dim(head_dim))
+      p.status = ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    p.empty = true;
+    return p;
+  }
+  p.status = check_common(q, k, v, o, lse, head_dim, dtype, softmax_scale, causal, window_left,
+                          window_right);
+  if (p.status != ATTN_OK) return p;
+  if (p.rows > kMaxRows || (long)seqlen * head_dim * 2 > kMaxSeqBytes) {
+    p.status = ATTN_ERR_TOO_LARGE;
+    return p;
+  }
+  int wl = window_left, wr = window_right;
+  p.mode = mask_mode(causal, seqlen, &wl, &wr);
+  const int br_big = block_rows(head_dim, true);
+  p.big = shape == 1 &&
+          (long)batch * heads * ((seqlen + br_big - 1) / br_big) >= xattn::BIG_TILE_MIN_WORK;
+  const int br = block_rows(head_dim, p.big);
+  xattn::FwdArgs& a = p.a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -120,41 +176,52 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.scale_log2 = softmax_scale * kLog2e;
   a.window_left = wl;
   a.window_right = wr;
-  const long n_work = (long)batch * heads * a.tiles_per_head;
-  return launch(head_dim, a, dtype, mode, big, n_work, stream);
+  a.num_splits = 1;
+  p.n_work = (long)batch * heads * a.tiles_per_head;
+  p.max_len = seqlen;
+  return p;
 }
 
-int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
-                    int heads, int head_dim, int dtype, float softmax_scale, int causal,
-                    int window_left, int window_right, void* stream) {
-  if (num_seqs < 0 || total_tokens < 0 || heads < 0 || max_seqlen < 0)
-    return ATTN_ERR_INVALID_ARG;
-  if (num_seqs == 0 || total_tokens == 0 || heads == 0) {
-    if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED_DTYPE;
-    if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
-    return ATTN_OK;
+Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                 int heads, int head_dim, int dtype, float softmax_scale, int causal,
+                 int window_left, int window_right, int shape) {
+  Plan p;
+  if (num_seqs < 0 || total_tokens < 0 || heads < 0 || max_seqlen < 0) {
+    p.status = ATTN_ERR_INVALID_ARG;
+    return p;
   }
-  int st = check_common(q, k, v, o, lse, head_dim, dtype, softmax_scale, causal, window_left,
-                        window_right);
-  if (st != ATTN_OK) return st;
-  if (!cu_seqlens) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(cu_seqlens, 4)) return ATTN_ERR_MISALIGNED;
-  if (max_seqlen < 1 || max_seqlen > total_tokens) return ATTN_ERR_INVALID_ARG;
-  if ((long)heads * total_tokens > kMaxRows) return ATTN_ERR_TOO_LARGE;
-  if ((long)max_seqlen * head_dim * 2 > kMaxSeqBytes) return ATTN_ERR_TOO_LARGE;
+  if (num_seqs == 0 || total_tokens == 0 || heads == 0) {
+    if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16)
+      p.status = ATTN_ERR_UNSUPPORTED_DTYPE;
+    else if (!supported_head_dim(head_dim))
+      p.status = ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    p.empty = true;
+    return p;
+  }
+  p.status = check_common(q, k, v, o, lse, head_dim, dtype, softmax_scale, causal, window_left,
+                          window_right);
+  if (p.status != ATTN_OK) return p;
+  if (!cu_seqlens) { p.status = ATTN_ERR_INVALID_ARG; return p; }
+  if (!aligned(cu_seqlens, 4)) { p.status = ATTN_ERR_MISALIGNED; return p; }
+  if (max_seqlen < 1 || max_seqlen > total_tokens) { p.status = ATTN_ERR_INVALID_ARG; return p; }
+  p.rows = (long)heads * total_tokens;
+  if (p.rows > kMaxRows || (long)max_seqlen * head_dim * 2 > kMaxSeqBytes) {
+    p.status = ATTN_ERR_TOO_LARGE;
+    return p;
+  }
   int wl = window_left, wr = window_right;
-  const int mode = mask_mode(causal, max_seqlen, &wl, &wr);
+  p.mode = mask_mode(causal, max_seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);
-  const bool big = (long)heads * (((long)total_tokens + br_big - 1) / br_big) >=
-                   xattn::BIG_TILE_MIN_WORK;
-  const int br = block_rows(head_dim, big);
+  p.big = shape == 1 && (long)heads * (((long)total_tokens + br_big - 1) / br_big) >=
+                            xattn::BIG_TILE_MIN_WORK;
+  const int br = block_rows(head_dim, p.big);
   // q-tile slots per head: an upper bound on sum_s ceil(len_s / br) that needs no lengths
   const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;
   const long by_max = (long)num_seqs * ((max_seqlen + br - 1) / br);
   const long slots = by_total < by_max ? by_total : by_max;
-  if (slots > std::numeric_limits<int>::max()) return ATTN_ERR_TOO_LARGE;
-  xattn::FwdArgs a{};
+  if (slots > std::numeric_limits<int>::max()) { p.status = ATTN_ERR_TOO_LARGE; return p; }
+  xattn::FwdArgs& a = p.a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -168,7 +235,151 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.scale_log2 = softmax_scale * kLog2e;
   a.window_left = wl;
   a.window_right = wr;
-  return launch(head_dim, a, dtype, mode, big, (long)heads * slots, stream);
+  a.num_splits = 1;
+  p.n_work = (long)heads * slots;
+  p.max_len = max_seqlen;
+  return p;
+}
+
+// Split count for num_splits = 0: enough work items to give every CU its resident share of
+// small-shape workgroups, keeping at least eight K/V tiles per split (shorter splits cost more
+// in merge traffic and per-workgroup set-up than they gain); 1 when the plain grid already
+// fills the chip.  Chosen by measurement on MI355X over dense and causal shapes.
+int auto_splits(long n_work, int max_len, int head_dim) {
+  const long target = (long)kNumCUs * resident_per_cu(head_dim);
+  if (n_work <= 0 || n_work >= target) return 1;
+  const int tiles = (max_len + small_tile_keys(head_dim) - 1) / small_tile_keys(head_dim);
+  long s = (target + n_work - 1) / n_work;
+  if (s > tiles / 8) s = tiles / 8;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace bytes for num_splits partial outputs of `rows` rows of head_dim fp32 plus their LSE.
+size_t workspace_bytes_for(long rows, int head_dim, int num_splits) {
+  if (num_splits <= 1) return 0;
+  return align256((size_t)num_splits * rows * head_dim * 4) +
+         align256((size_t)num_splits * rows * 4);
+}
+
+// Run a plan as split-KV with the given split count (> 1) in the caller's workspace.
+int run_split(Plan& p, int head_dim, int dtype, int num_splits, void* workspace,
+              size_t workspace_size, void* stream) {
+  const size_t need = workspace_bytes_for(p.rows, head_dim, num_splits);
+  if (!workspace || !aligned(workspace, 256) || workspace_size < need)
+    return ATTN_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  p.a.num_splits = num_splits;
+  p.a.split_rows = p.rows;
+  p.a.o_part = reinterpret_cast<float*>(ws);
+  p.a.lse_part =
+      reinterpret_cast<float*>(ws + align256((size_t)num_splits * p.rows * head_dim * 4));
+  xattn::MergeArgs m{};
+  m.o_part = p.a.o_part;
+  m.lse_part = p.a.lse_part;
+  m.o = p.a.o;
+  m.lse = p.a.lse;
+  m.rows = p.rows;
+  m.num_splits = num_splits;
+  return launch_split(head_dim, p.a, m, dtype, p.mode, p.n_work, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+             int heads, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
+             int window_left, int window_right, void* stream) {
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
+                      causal, window_left, window_right, 1);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int heads, int head_dim, int dtype, float softmax_scale, int causal,
+                    int window_left, int window_right, void* stream) {
+  Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, heads,
+                       head_dim, dtype, softmax_scale, causal, window_left, window_right, 1);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
+}
+
+int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim) {
+  if (batch <= 0 || heads <= 0 || seqlen <= 0 || !supported_head_dim(head_dim)) return 1;
+  const int br = block_rows(head_dim, false);
+  const long n_work = (long)batch * heads * ((seqlen + br - 1) / br);
+  return auto_splits(n_work, seqlen, head_dim);
+}
+
+size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
+                                       int num_splits) {
+  if (batch <= 0 || heads <= 0 || seqlen <= 0 || !supported_head_dim(head_dim) ||
+      num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  const int s = num_splits ? num_splits : attn_fwd_splitkv_num_splits(batch, heads, seqlen,
+                                                                      head_dim);
+  return workspace_bytes_for((long)batch * heads * seqlen, head_dim, s);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads, int seqlen, int head_dim, int dtype,
+                     float softmax_scale, int causal, int window_left, int window_right,
+                     int num_splits, void* workspace, size_t workspace_size, void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
+                      causal, window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  if (s == 1)
+    return attn_fwd(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
+                    causal, window_left, window_right, stream);
+  return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
+}
+
+int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
+                                       int heads, int head_dim) {
+  if (num_seqs <= 0 || max_seqlen <= 0 || total_tokens <= 0 || heads <= 0 ||
+      !supported_head_dim(head_dim))
+    return 1;
+  const int br = block_rows(head_dim, false);
+  const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;
+  const long by_max = (long)num_seqs * ((max_seqlen + br - 1) / br);
+  return auto_splits((long)heads * (by_total < by_max ? by_total : by_max), max_seqlen,
+                     head_dim);
+}
+
+size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int total_tokens,
+                                              int heads, int head_dim, int num_splits) {
+  if (num_seqs <= 0 || max_seqlen <= 0 || total_tokens <= 0 || heads <= 0 ||
+      !supported_head_dim(head_dim) || num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  const int s = num_splits ? num_splits
+                           : attn_fwd_varlen_splitkv_num_splits(num_seqs, max_seqlen,
+                                                                total_tokens, heads, head_dim);
+  return workspace_bytes_for((long)heads * total_tokens, head_dim, s);
+}
+
+int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                            int total_tokens, int heads, int head_dim, int dtype,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            int num_splits, void* workspace, size_t workspace_size,
+                            void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, heads,
+                       head_dim, dtype, softmax_scale, causal, window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  if (s == 1)
+    return attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
+                           heads, head_dim, dtype, softmax_scale, causal, window_left,
+                           window_right, stream);
+  return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 
 const char* attn_status_string(int status) {

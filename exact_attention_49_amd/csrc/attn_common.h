@@ -36,6 +36,7 @@ namespace xattn {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -59,6 +60,12 @@ struct FwdArgs {
   float scale_log2;           // softmax_scale * log2(e): scores are exponentiated base 2
   int window_left;            // -1 = unbounded (MASK_WINDOW only)
   int window_right;           // -1 = unbounded (MASK_WINDOW only; causal folded in as 0)
+  // split-KV mode only: the key tiles of each q-tile are shared out among num_splits work
+  // items, which write normalised fp32 partial outputs and their LSE instead of o / lse
+  int num_splits;             // 1 outside split-KV mode
+  long split_rows;            // rows of one split's partial arrays (= rows of o)
+  float* o_part;              // [num_splits][split_rows][D]
+  float* lse_part;            // [num_splits][split_rows], natural log
 };
 
 // The running max is only moved when a tile's row max exceeds it by more than this (in log2
@@ -213,15 +220,22 @@ struct Work {
   int tile;    // q-tile index within the sequence
   int seqlen;  // rows (= keys) of the sequence
   long row0;   // index of the sequence's token 0 in the [*, D] row space of q/k/v/o and lse
+  int split;   // split-KV: which share of the q-tile's key tiles (0 otherwise)
 };
 
-// Map this workgroup to (q-tile, head, batch | sequence).  Dense batches: heads of all batch
-// entries in order, q-tiles of a head consecutive (heaviest first for masked modes, whose
-// later q-tiles see more keys).  Packed batches: the q-tile slots of a head walk the sequences
-// in order; slots past the last tile are unused.  Returns false for an unused slot.
-template <int BR, int MODE>
+// Map this workgroup to (q-tile, head, batch | sequence) and, in split-KV mode, a split.
+// Dense batches: heads of all batch entries in order, q-tiles of a head consecutive (heaviest
+// first for masked modes, whose later q-tiles see more keys).  Packed batches: the q-tile
+// slots of a head walk the sequences in order; slots past the last tile are unused.  Returns
+// false for an unused slot.
+template <int BR, int MODE, bool SPLIT = false>
 __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  int wid = xcd_remap(blockIdx.x, gridDim.x);
+  w.split = 0;
+  if constexpr (SPLIT) {  // the splits of one q-tile are neighbours (they share its Q rows)
+    w.split = wid % a.num_splits;
+    wid /= a.num_splits;
+  }
   const int per = a.tiles_per_head;
   if (a.cu_seqlens == nullptr) {
     const int bh = wid / per, t = wid - bh * per;
@@ -249,6 +263,15 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
     c_prev = c_next;
   }
   return false;
+}
+
+// Split-KV: restrict the key-tile range [t_lo, t_lo + n) of a q-tile to the share of split
+// `split` (contiguous, as equal as integer division allows; possibly empty).
+__device__ __forceinline__ void split_tiles(int split, int num_splits, int& t_lo, int& n) {
+  const int a0 = (int)((long)n * split / num_splits);
+  const int a1 = (int)((long)n * (split + 1) / num_splits);
+  t_lo += a0;
+  n = a1 - a0;
 }
 
 // Effective window bounds of a mask mode (-1 = unbounded).
@@ -509,6 +532,33 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, long row0, int qrow
     }
   if (a.lse != nullptr && hh == 0)
     a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
+}
+
+// Split-KV epilogue for one 32-row block: the normalised fp32 partial O = O / l and its
+// natural-log LSE go to split `split` of the partial arrays (a row with nothing visible in
+// this split gets O = 0, LSE = -inf).  All lanes must call it; rows past the end of the
+// sequence are not stored.
+template <int D>
+__device__ __forceinline__ void store_rows_partial(const FwdArgs& a, int split, long row0,
+                                                   int qrow, int seqlen, int hh,
+                                                   const f32x16 (&o)[D / 32], float m_run,
+                                                   float l_run) {
+  constexpr float LN2 = 0.693147180559945309f;
+  const float lt = halves_sum(l_run);
+  if (qrow >= seqlen) return;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const long row = (long)split * a.split_rows + row0 + qrow;
+  float* dst = a.o_part + row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& x = o[db];
+      const f32x4 val = {x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv, x[4 * g4 + 2] * inv,
+                         x[4 * g4 + 3] * inv};
+      *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
+    }
+  if (hh == 0) a.lse_part[row] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
 }  // namespace xattn

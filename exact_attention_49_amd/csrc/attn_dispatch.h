@@ -8,6 +8,7 @@
 #include "attn_fwd_kernel.h"
 #include "attn_fwd_pingpong.h"
 #include "attn_fwd_wide.h"
+#include "attn_merge.h"
 
 namespace xattn {
 
@@ -46,45 +47,65 @@ template <> struct TileCfg<512> {
 // Workgroups the big shape must yield before it is preferred (4 per CU on 256 CUs).
 constexpr long BIG_TILE_MIN_WORK = 1024;
 
-template <bool BF16, int D, int MODE, class S> struct Launch;
-template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong> {
+template <bool BF16, int D, int MODE, class S, bool SPLIT> struct Launch;
+template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong, false> {
   static void go(const FwdArgs& a, int n_work, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_pp_kernel<BF16, D, MODE>), dim3(n_work),
                        dim3(PingPongShape::NT), 0, s, a);
   }
 };
-template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UseWide> {
+template <bool BF16, int D, int MODE, bool SPLIT> struct Launch<BF16, D, MODE, UseWide, SPLIT> {
   static void go(const FwdArgs& a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_wide_kernel<BF16, D, MODE>), dim3(n_work), dim3(WideShape::NT),
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<BF16, D, MODE, SPLIT>), dim3(n_work),
+                       dim3(WideShape::NT), 0, s, a);
+  }
+};
+template <bool BF16, int D, int MODE, class T, bool SPLIT>
+struct Launch<BF16, D, MODE, UseGeneric<T>, SPLIT> {
+  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
+    hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, MODE, T, SPLIT>), dim3(n_work), dim3(T::NT),
                        0, s, a);
   }
 };
-template <bool BF16, int D, int MODE, class T> struct Launch<BF16, D, MODE, UseGeneric<T>> {
-  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, MODE, T>), dim3(n_work), dim3(T::NT), 0, s,
-                       a);
-  }
-};
 
-template <int D, class S>
+template <int D, class S, bool SPLIT = false>
 hipError_t launch_shape(const FwdArgs& a, bool bf16, int mode, int n_work, hipStream_t s) {
   if (bf16) {
-    if (mode == MASK_NONE) Launch<true, D, MASK_NONE, S>::go(a, n_work, s);
-    else if (mode == MASK_CAUSAL) Launch<true, D, MASK_CAUSAL, S>::go(a, n_work, s);
-    else Launch<true, D, MASK_WINDOW, S>::go(a, n_work, s);
+    if (mode == MASK_NONE) Launch<true, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
+    else if (mode == MASK_CAUSAL) Launch<true, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
+    else Launch<true, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
   } else {
-    if (mode == MASK_NONE) Launch<false, D, MASK_NONE, S>::go(a, n_work, s);
-    else if (mode == MASK_CAUSAL) Launch<false, D, MASK_CAUSAL, S>::go(a, n_work, s);
-    else Launch<false, D, MASK_WINDOW, S>::go(a, n_work, s);
+    if (mode == MASK_NONE) Launch<false, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
+    else if (mode == MASK_CAUSAL) Launch<false, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
+    else Launch<false, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
   }
   return hipGetLastError();
 }
 
-// Host launcher for one head dim (explicitly specialised per head dim in its own translation
-// unit).  `big` selects the shape; the caller sizes the grid with that shape's BR.
+// Split-KV runs on the small shape of a head dim (the one for grids too small to fill the
+// chip); the merge is one wave per row, four rows per workgroup.
+template <int D>
+hipError_t launch_merge_shape(const MergeArgs& m, bool bf16, hipStream_t s) {
+  const long blocks = (m.rows + 3) / 4;
+  if (bf16)
+    hipLaunchKernelGGL((attn_merge_kernel<true, D>), dim3((unsigned)blocks), dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<false, D>), dim3((unsigned)blocks), dim3(256), 0, s, m);
+  return hipGetLastError();
+}
+
+// Host launchers for one head dim (explicitly specialised per head dim in its own translation
+// unit).  launch_fwd: `big` selects the shape; the caller sizes the grid with that shape's BR.
+// launch_fwd_split: the split-KV sweep on the small shape (grid = work items x splits).
+// launch_merge: the split-KV merge.
 template <int D>
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int mode, bool big, int n_work,
                       hipStream_t stream);
+template <int D>
+hipError_t launch_fwd_split(const FwdArgs& a, bool bf16, int mode, int n_work,
+                            hipStream_t stream);
+template <int D>
+hipError_t launch_merge(const MergeArgs& m, bool bf16, hipStream_t stream);
 
 #define XATTN_DEFINE_LAUNCHER(D)                                                            \
   template <>                                                                               \
@@ -93,6 +114,15 @@ hipError_t launch_fwd(const FwdArgs& a, bool bf16, int mode, bool big, int n_wor
     if (big || std::is_same<TileCfg<D>::Big, TileCfg<D>::Small>::value)                     \
       return launch_shape<D, TileCfg<D>::Big>(a, bf16, mode, n_work, stream);               \
     return launch_shape<D, TileCfg<D>::Small>(a, bf16, mode, n_work, stream);               \
+  }                                                                                         \
+  template <>                                                                               \
+  hipError_t launch_fwd_split<D>(const FwdArgs& a, bool bf16, int mode, int n_work,         \
+                                 hipStream_t stream) {                                      \
+    return launch_shape<D, TileCfg<D>::Small, true>(a, bf16, mode, n_work, stream);         \
+  }                                                                                         \
+  template <>                                                                               \
+  hipError_t launch_merge<D>(const MergeArgs& m, bool bf16, hipStream_t stream) {           \
+    return launch_merge_shape<D>(m, bf16, stream);                                          \
   }
 
 }  // namespace xattn

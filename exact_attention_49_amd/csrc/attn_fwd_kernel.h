@@ -19,7 +19,9 @@ struct Tile {
   static constexpr int NT = NW * 64;  // threads per workgroup
 };
 
-template <bool BF16, int D, int MODE, class C>
+// SPLIT: split-KV mode (the workgroup sweeps its split's share of the key tiles and writes
+// fp32 partial results; see FwdArgs).
+template <bool BF16, int D, int MODE, class C, bool SPLIT = false>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   constexpr int BC = C::BC, STAGES = C::STAGES;
@@ -38,7 +40,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   Work w;
-  if (!decode_work<BR, MODE>(a, w)) return;
+  if (!decode_work<BR, MODE, SPLIT>(a, w)) return;
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);
@@ -49,7 +51,9 @@ void attn_fwd_kernel(FwdArgs a) {
   int k_lo = 0, k_hi = seqlen - 1;                     // keys any valid row can see
   if (wl >= 0) k_lo = max(0, q0 - wl);
   if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
-  const int t_lo = k_lo / BC, t_hi = k_hi / BC;
+  int t_lo = k_lo / BC, n_tiles = k_hi / BC - t_lo + 1;
+  if constexpr (SPLIT) split_tiles(w.split, a.num_splits, t_lo, n_tiles);
+  const int t_hi = t_lo + n_tiles - 1;
 
   const bool wave_active = qw0 < seqlen;
   const int qw_last = min(qw0 + 32, seqlen) - 1;
@@ -133,8 +137,10 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // ---- the sweep over K/V tiles ---------------------------------------------------------
   if constexpr (STAGES == 2) {
-    gload(t_lo);
-    lstore(0);
+    if (n_tiles > 0) {
+      gload(t_lo);
+      lstore(0);
+    }
     __syncthreads();
     for (int t = t_lo; t <= t_hi; ++t) {
       const int s = (t - t_lo) & 1;
@@ -153,7 +159,11 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  if (wave_active) store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  if (!wave_active) return;
+  if constexpr (SPLIT)
+    store_rows_partial<D>(a, w.split, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  else
+    store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
 }
 
 }  // namespace xattn

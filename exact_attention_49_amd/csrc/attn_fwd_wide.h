@@ -123,7 +123,9 @@ __device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, i
     a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
-template <bool BF16, int D, int MODE>
+// SPLIT: split-KV mode (the workgroup sweeps its split's share of the key tiles and writes
+// fp32 partial results; see FwdArgs).
+template <bool BF16, int D, int MODE, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_fwd_wide_kernel(FwdArgs a) {
   constexpr int BR = WideShape::BR, BC = WideShape::BC, NT = WideShape::NT;
@@ -147,7 +149,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   Work w;
-  if (!decode_work<BR, MODE>(a, w)) return;
+  if (!decode_work<BR, MODE, SPLIT>(a, w)) return;
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);
@@ -158,8 +160,9 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   int k_lo = 0, k_hi = seqlen - 1;
   if (wl >= 0) k_lo = max(0, q0 - wl);
   if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
-  const int t_lo = k_lo / BC;
-  const int n = k_hi / BC - t_lo + 1;
+  int t_lo = k_lo / BC;
+  int n = k_hi / BC - t_lo + 1;
+  if constexpr (SPLIT) split_tiles(w.split, a.num_splits, t_lo, n);
 
   const bool wave_active = qw0 < seqlen;
   const int qw_last = min(qw0 + 32, seqlen) - 1;
@@ -281,7 +284,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   const int t_hi = t_lo + n - 1;
   const unsigned k0a = lds_address(k_lds0), k1a = lds_address(k_lds1);
   const unsigned v0a = lds_address(v_lds0), v1a = lds_address(v_lds1);
-  load_tile(t_lo, k0a, v0a);
+  if (n > 0) load_tile(t_lo, k0a, v0a);
   wait_vmem();
   block_barrier();
   for (int t = t_lo; t <= t_hi; t += 2) {
@@ -298,7 +301,11 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   agpr_settle(oacc);
   char* const region = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
   static_assert(TILEB == 32 * ROWB, "a tile buffer holds one wave's 32 output rows");
-  if (wave_active) store_rows_staged<BF16, D>(a, w.row0, qw0, seqlen, lane, oacc, m_run, l_run, region);
+  if (!wave_active) return;
+  if constexpr (SPLIT)
+    store_rows_partial<D>(a, w.split, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  else
+    store_rows_staged<BF16, D>(a, w.row0, qw0, seqlen, lane, oacc, m_run, l_run, region);
 }
 
 }  // namespace xattn

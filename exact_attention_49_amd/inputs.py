@@ -44,6 +44,7 @@ class Workload:
     window_left: int = -1
     window_right: int = -1
     value_scale: float = 1.0
+    splitkv: bool = False   # run through the split-KV entry point
     note: str = field(default="", compare=False)
 
     @property
@@ -78,6 +79,11 @@ WORKLOADS = {
         Workload("dense_fp16_d512_n4096", batch=1, heads=8, seqlen=4096, head_dim=512,
                  dtype="fp16", causal=False, seed=4905,
                  note="B=1 H=8 N=4096 d=512 fp16 non-causal"),
+        # a long problem with few heads: its plain grid (2 x 128 q-tiles) cannot fill the
+        # chip, the case split-KV is for
+        Workload("splitkv_bf16_d128_h2_n16384", batch=1, heads=2, seqlen=16384,
+                 head_dim=128, dtype="bf16", causal=True, seed=4906, splitkv=True,
+                 note="B=1 H=2 N=16384 d=128 bf16 causal, split-KV (low occupancy)"),
     ]
 }
 

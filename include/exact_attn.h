@@ -34,6 +34,7 @@
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -89,6 +90,51 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
                     int heads, int head_dim, int dtype, float softmax_scale,
                     int causal, int window_left, int window_right, void* stream);
+
+/*
+ * Split-KV variants, for problems whose plain grid cannot fill the GPU (few heads and q-tiles
+ * over long sequences).  The key tiles that every q-tile sees are shared out among num_splits
+ * work items; each writes a normalised fp32 partial output O_s and the natural-log LSE_s of
+ * the scores it saw into a caller-provided workspace, and a second kernel merges them:
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * The result is the same function as attn_fwd / attn_fwd_varlen, up to rounding (page
+ * "flash_fwd_kernel.h" @c272619: split-KV work items, n_split_idx; the merge is the
+ * log-sum-exp identity written out).
+ *   num_splits     : 1..64, or 0 to let the library choose.  A count of 1 (chosen or given)
+ *                    runs the plain kernels and leaves the workspace untouched (it may then be
+ *                    NULL).
+ *   workspace      : DEVICE memory owned by the caller, 256-byte aligned, of at least
+ *                    workspace_size bytes, and workspace_size must be at least what the
+ *                    matching *_workspace_size function returns for the same sizes and
+ *                    num_splits; otherwise ATTN_ERR_INVALID_ARG.  Its contents on entry do not
+ *                    matter and on exit are unspecified; two calls in flight at once must not
+ *                    share a workspace.
+ * All other arguments, layouts and errors are those of attn_fwd / attn_fwd_varlen.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int heads, int seqlen, int head_dim, int dtype,
+                     float softmax_scale, int causal, int window_left, int window_right,
+                     int num_splits, void* workspace, size_t workspace_size, void* stream);
+
+int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                            int total_tokens, int heads, int head_dim, int dtype,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            int num_splits, void* workspace, size_t workspace_size,
+                            void* stream);
+
+/* Workspace bytes the split-KV calls need for these sizes and num_splits (0 = the count the
+ * library would choose).  0 when no workspace is needed (one split) or the arguments are
+ * invalid.  Host-only: no device is touched. */
+size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
+                                       int num_splits);
+size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int total_tokens,
+                                              int heads, int head_dim, int num_splits);
+
+/* The split count num_splits = 0 selects for these sizes (1 = no split).  Host-only. */
+int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim);
+int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
+                                       int heads, int head_dim);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

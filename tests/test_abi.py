@@ -108,3 +108,58 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(binding.AttnError, match="GPU tensor"):
         binding.attn_fwd(x, x, x)
+
+
+# ---- split-KV entry points (host-side validation and workspace sizing only) ----------------
+
+def call_dense_split(lib, ns=2, ws=A, wsb=1 << 30, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=None, b=1, h=1, n=4096, d=128, dtype=1, scale=SCALE,
+                causal=0, wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                args["b"], args["h"], args["n"], args["d"], args["dtype"],
+                                args["scale"], args["causal"], args["wl"], args["wr"], ns, ws,
+                                wsb, None)
+
+
+def test_splitkv_workspace_size_formula(lib):
+    # ns partial rows of d fp32 values plus ns LSE values per row, each part 256-byte aligned
+    def expect(rows, d, ns):
+        up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        return up(ns * rows * d * 4) + up(ns * rows * 4)
+    assert lib.attn_fwd_splitkv_workspace_size(2, 3, 1000, 128, 4) == expect(6000, 128, 4)
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 77, 64, 3) == expect(77, 64, 3)
+    assert lib.attn_fwd_varlen_splitkv_workspace_size(5, 300, 1000, 4, 256, 2) == \
+        expect(4000, 256, 2)
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 1) == 0      # one split
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 96, 2) == 0       # bad head dim
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 65) == 0     # too many splits
+    assert lib.attn_fwd_splitkv_workspace_size(0, 1, 4096, 128, 2) == 0      # empty
+
+
+def test_splitkv_automatic_count(lib):
+    # a grid that fills the chip needs no split; a single long head does
+    assert lib.attn_fwd_splitkv_num_splits(2, 32, 8192, 128) == 1
+    s = lib.attn_fwd_splitkv_num_splits(1, 1, 16384, 128)
+    assert 2 <= s <= 64
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, 0) == \
+        lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, s)
+    # never fewer than eight key tiles per split
+    assert lib.attn_fwd_splitkv_num_splits(1, 1, 256, 128) == 1
+    assert lib.attn_fwd_splitkv_num_splits(1, 1, 4096, 128) == 8
+    assert lib.attn_fwd_varlen_splitkv_num_splits(2, 8192, 9000, 1, 64) >= 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ns=-1), 1), (dict(ns=65), 1),                      # split count
+    (dict(ws=None), 1), (dict(ws=A + 64), 1), (dict(wsb=1024), 1),   # workspace
+    (dict(q=None), 1), (dict(d=96), 2), (dict(dtype=5), 3), (dict(o=A + 2), 4),
+])
+def test_splitkv_rejects_bad_arguments(lib, kw, status):
+    assert call_dense_split(lib, **kw) == status
+
+
+def test_splitkv_one_split_needs_no_workspace(lib):
+    # with one split the plain kernels run; validation still happens on the host first
+    assert call_dense_split(lib, ns=1, ws=None, wsb=0, d=96) == 2
+    assert call_dense_split(lib, ns=0, ws=None, wsb=0, b=0) == 0   # empty problem

@@ -346,6 +346,26 @@ def test_sampled_rows_match_full():
     assert np.allclose(lse_r, lse[idx[:, 0], idx[:, 1]], atol=1e-13)
 
 
+def test_split_merge_identity():
+    """Split-KV reading: attention over all keys equals the merge of attention over disjoint
+    key ranges, LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, with an empty
+    range (LSE_s = -inf) contributing nothing.  Checked on the oracle, range by range."""
+    q, k, v = (rnd((12, 8), s) for s in (41, 42, 43))
+    o_full, lse_full = oracle.attention_head(q, k, v, 0.7)
+    for cuts in ([0, 5, 12], [0, 1, 2, 12], [0, 12, 12], [0, 3, 3, 9, 12]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if a == b:
+                parts.append((np.zeros_like(o_full), np.full(12, -np.inf)))
+            else:
+                parts.append(oracle.attention_head(q, k[a:b], v[a:b], 0.7))
+        lse_s = np.stack([p[1] for p in parts])
+        lse = np.log(np.sum(np.exp(lse_s), axis=0))
+        o = sum(np.exp(ls - lse)[:, None] * o_s for o_s, ls in parts)
+        assert np.allclose(lse, lse_full, atol=1e-12)
+        assert np.allclose(o, o_full, atol=1e-12)
+
+
 def test_flops_formula():
     assert oracle.flops_dense(2, 32, 8192, 128, True) == 2 * 2 * 32 * 8192 ** 2 * 128
     assert oracle.flops_dense(1, 8, 4096, 512, False) == 4 * 8 * 4096 ** 2 * 512
