@@ -26,6 +26,10 @@ alignment), key j is visible to query i iff
     and (window_right < 0 or j <= i + delta + window_right).
 A window bound of -1 means unbounded.  `causal` is the local mask with window_right = 0.
 
+Grouped-query attention: K and V may have fewer heads than Q (a divisor of its head count);
+query head h then uses key/value head h // (heads_q // heads_kv) (page
+"mainloop_bwd_sm90_tma_gmma_ws.hpp", the qhead_per_khead division).
+
 Empty rows (no visible key): O_i = 0 and LSE_i = -inf (page "flash_fwd_kernel.h" @26a6e0a,
 consumer loop: a tile with no key block to visit stores zeros through `store_zero`).
 
@@ -117,19 +121,30 @@ def attention_head(q, k, v, scale: float, causal: bool = False, window_left: int
     return _masked_softmax_times_v(s, vis, v)
 
 
+def _kv_group(heads_q: int, heads_kv: int) -> int:
+    """Query heads per key/value head.  Grouped-query attention (page
+    "mainloop_bwd_sm90_tma_gmma_ws.hpp", the qhead_per_khead division): query head h uses
+    key/value head h // group; group 1 is plain multi-head attention."""
+    if heads_kv < 1 or heads_q % heads_kv != 0:
+        raise ValueError("the key/value head count must divide the query head count")
+    return heads_q // heads_kv
+
+
 def attention_dense(q, k, v, scale: float, causal: bool = False, window_left: int = -1,
                     window_right: int = -1):
-    """Dense batch: Q, K, V [B, H, N, d] (page "flash_attn_mma_tiling_qk.cu", header comment)
-    -> O [B, H, N, d] and LSE [B, H, N], both float64."""
+    """Dense batch: Q [B, H, N, d], K and V [B, Hkv, N, d] with Hkv dividing H (Hkv = H in
+    the plain case; page "flash_attn_mma_tiling_qk.cu", header comment) -> O [B, H, N, d] and
+    LSE [B, H, N], both float64."""
     q = np.asarray(q)
     bsz, nh, n, _ = q.shape
+    g = _kv_group(nh, np.asarray(k).shape[1])
     dv = np.asarray(v).shape[-1]
     o = np.empty((bsz, nh, n, dv), dtype=np.float64)
     lse = np.empty((bsz, nh, n), dtype=np.float64)
     for b in range(bsz):
         for h in range(nh):
-            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal,
-                                                window_left, window_right)
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h // g], v[b, h // g], scale,
+                                                causal, window_left, window_right)
     return o, lse
 
 
@@ -142,12 +157,14 @@ def _check_cu_seqlens(cu_seqlens, total: int) -> np.ndarray:
 
 def attention_varlen(q, k, v, cu_seqlens, scale: float, causal: bool = False,
                      window_left: int = -1, window_right: int = -1):
-    """Packed variable-length batch: Q, K, V [H, total_tokens, d]; sequence s owns tokens
+    """Packed variable-length batch: Q [H, total_tokens, d], K and V [Hkv, total_tokens, d]
+    (Hkv dividing H, as in `attention_dense`); sequence s owns tokens
     [cu_seqlens[s], cu_seqlens[s+1]) (page "mainloop_bwd_sm90_tma_gmma_ws.hpp", get_seqlen_q/k:
     the length is the difference of consecutive cu_seqlens entries).  Each sequence attends
     only within itself.  Returns O [H, total, d] and LSE [H, total], float64."""
     q = np.asarray(q)
     nh, total, _ = q.shape
+    g = _kv_group(nh, np.asarray(k).shape[0])
     dv = np.asarray(v).shape[-1]
     cu = _check_cu_seqlens(cu_seqlens, total)
     o = np.zeros((nh, total, dv), dtype=np.float64)
@@ -157,8 +174,8 @@ def attention_varlen(q, k, v, cu_seqlens, scale: float, causal: bool = False,
         if b == a:
             continue
         for h in range(nh):
-            o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[h, a:b], v[h, a:b], scale,
-                                                    causal, window_left, window_right)
+            o[h, a:b], lse[h, a:b] = attention_head(q[h, a:b], k[h // g, a:b], v[h // g, a:b],
+                                                    scale, causal, window_left, window_right)
     return o, lse
 
 
@@ -180,12 +197,13 @@ def attention_rows_dense(q, k, v, index, scale: float, causal: bool = False,
     evaluated only at the requested rows.  Returns (o [R, d], lse [R]) float64."""
     idx = np.asarray(index, dtype=np.int64).reshape(-1, 3)
     q = np.asarray(q)
+    g = _kv_group(q.shape[1], np.asarray(k).shape[1])
     o = np.empty((idx.shape[0], np.asarray(v).shape[-1]), dtype=np.float64)
     lse = np.empty(idx.shape[0], dtype=np.float64)
     for (b, h) in sorted({(int(b), int(h)) for b, h, _ in idx}):
         sel = np.nonzero((idx[:, 0] == b) & (idx[:, 1] == h))[0]
-        o[sel], lse[sel] = _rows_one_head(q[b, h], k[b, h], v[b, h], idx[sel, 2], scale,
-                                          causal, window_left, window_right)
+        o[sel], lse[sel] = _rows_one_head(q[b, h], k[b, h // g], v[b, h // g], idx[sel, 2],
+                                          scale, causal, window_left, window_right)
     return o, lse
 
 
@@ -195,6 +213,7 @@ def attention_rows_varlen(q, k, v, cu_seqlens, index, scale: float, causal: bool
     Same definition as `attention_varlen`, evaluated only at the requested rows."""
     idx = np.asarray(index, dtype=np.int64).reshape(-1, 2)
     q = np.asarray(q)
+    g = _kv_group(q.shape[0], np.asarray(k).shape[0])
     cu = _check_cu_seqlens(cu_seqlens, q.shape[1])
     o = np.empty((idx.shape[0], np.asarray(v).shape[-1]), dtype=np.float64)
     lse = np.empty(idx.shape[0], dtype=np.float64)
@@ -202,8 +221,9 @@ def attention_rows_varlen(q, k, v, cu_seqlens, index, scale: float, causal: bool
     for (h, s) in sorted({(int(h), int(s)) for h, s in zip(idx[:, 0], seq_of)}):
         sel = np.nonzero((idx[:, 0] == h) & (seq_of == s))[0]
         a, b = int(cu[s]), int(cu[s + 1])
-        o[sel], lse[sel] = _rows_one_head(q[h, a:b], k[h, a:b], v[h, a:b], idx[sel, 1] - a,
-                                          scale, causal, window_left, window_right)
+        o[sel], lse[sel] = _rows_one_head(q[h, a:b], k[h // g, a:b], v[h // g, a:b],
+                                          idx[sel, 1] - a, scale, causal, window_left,
+                                          window_right)
     return o, lse
 
 

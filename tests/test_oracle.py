@@ -181,6 +181,68 @@ def test_oracle_matches_torch_sdpa_float64(mask):
     assert np.allclose(o, ref, atol=1e-10, rtol=0)
 
 
+@pytest.mark.parametrize("mask", MASKS[:4])
+@pytest.mark.parametrize("nh,nkv", [(4, 2), (6, 1), (6, 3), (3, 3)])
+def test_gqa_matches_torch_sdpa_enable_gqa(mask, nh, nkv):
+    """Grouped-query attention against torch's own grouped SDPA (float64, CPU), which gives
+    query head h the key/value head h // (H / Hkv), the same grouping as the qhead_per_khead
+    division of page "mainloop_bwd_sm90_tma_gmma_ws.hpp"."""
+    bsz, n, d = 2, 29, 8
+    q, k, v = rnd((bsz, nh, n, d), 11), rnd((bsz, nkv, n, d), 12), rnd((bsz, nkv, n, d), 13)
+    scale = 0.3
+    vis = torch.from_numpy(oracle.visibility(n, n, mask["causal"], mask["wl"], mask["wr"]))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=vis,
+        scale=float(np.float32(scale)), enable_gqa=True).numpy()
+    o, _ = oracle.attention_dense(q, k, v, scale, mask["causal"], mask["wl"], mask["wr"])
+    assert np.allclose(o, ref, atol=1e-10, rtol=0)
+
+
+def test_gqa_head_mapping_is_grouped_not_strided():
+    """With 4 query heads on 2 key/value heads, query heads 0 and 1 share key/value head 0:
+    their outputs match the plain attention of that head, and differ from head 1's."""
+    q, k, v = rnd((1, 4, 10, 4), 14), rnd((1, 2, 10, 4), 15), rnd((1, 2, 10, 4), 16)
+    o, lse = oracle.attention_dense(q, k, v, 0.5, True)
+    for h in range(4):
+        o_h, lse_h = oracle.attention_head(q[0, h], k[0, h // 2], v[0, h // 2], 0.5, True)
+        o_x, _ = oracle.attention_head(q[0, h], k[0, 1 - h // 2], v[0, 1 - h // 2], 0.5, True)
+        assert np.array_equal(o[0, h], o_h) and np.array_equal(lse[0, h], lse_h)
+        assert not np.allclose(o[0, h], o_x)
+
+
+def test_gqa_rejects_non_divisor_head_count():
+    q, k = rnd((1, 4, 5, 4), 17), rnd((1, 3, 5, 4), 18)
+    with pytest.raises(ValueError):
+        oracle.attention_dense(q, k, k, 0.5)
+    with pytest.raises(ValueError):
+        oracle.attention_varlen(q[0], k[0], k[0], np.array([0, 5]), 0.5)
+
+
+def test_gqa_varlen_and_sampled_rows():
+    """Varlen GQA is dense GQA per sequence; sampled rows equal the full result."""
+    lens = [9, 0, 14, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    qv, kv, vv = rnd((6, cu[-1], 4), 19), rnd((2, cu[-1], 4), 20), rnd((2, cu[-1], 4), 21)
+    o, lse = oracle.attention_varlen(qv, kv, vv, cu, 0.6, True, 5, 0)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        od, ld = oracle.attention_dense(qv[None, :, a:b], kv[None, :, a:b], vv[None, :, a:b],
+                                        0.6, True, 5, 0)
+        assert np.array_equal(o[:, a:b], od[0]) and np.array_equal(lse[:, a:b], ld[0])
+    idx = np.array([[0, 0], [5, 8], [2, 9], [3, 22], [4, 26], [1, 13]])
+    o_r, lse_r = oracle.attention_rows_varlen(qv, kv, vv, cu, idx, 0.6, True, 5, 0)
+    assert np.allclose(o_r, o[idx[:, 0], idx[:, 1]], atol=1e-13)
+    assert np.allclose(lse_r, lse[idx[:, 0], idx[:, 1]], atol=1e-13)
+    q, k, v = rnd((2, 6, 30, 4), 22), rnd((2, 3, 30, 4), 23), rnd((2, 3, 30, 4), 24)
+    o, lse = oracle.attention_dense(q, k, v, 0.6, False, 3, 2)
+    idx = np.array([[0, 0, 0], [1, 5, 29], [0, 3, 11], [1, 2, 4]])
+    o_r, lse_r = oracle.attention_rows_dense(q, k, v, idx, 0.6, False, 3, 2)
+    assert np.allclose(o_r, o[idx[:, 0], idx[:, 1], idx[:, 2]], atol=1e-13)
+    assert np.allclose(lse_r, lse[idx[:, 0], idx[:, 1], idx[:, 2]], atol=1e-13)
+
+
 # ---------------------------------------------------------------------------------------------
 # Hand-derived values
 # ---------------------------------------------------------------------------------------------
