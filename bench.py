@@ -2,8 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step = one forward pass (one attn_fwd / attn_fwd_varlen call; for the split-KV workload
-one attn_fwd_splitkv call, which runs the split sweep and the merge) over the workload's
+One step = one forward pass (one attn_fwd / attn_fwd_varlen call, attn_fwd_gqa for the
+grouped-query workload; for the split-KV workload one attn_fwd_splitkv call, which runs the
+split sweep and the merge) over the workload's
 inputs, which are resident in HBM before timing starts.  W untimed steps, then exactly K timed
 steps between two device synchronisations.  Rank 0 prints one JSON line:
 
@@ -77,9 +78,9 @@ def workload_flops(w, cu=None) -> float:
 
 def workload_bytes(w, cu=None) -> float:
     """Algorithmic HBM bytes per launch: Q, K, V read once, O written once (2 B each) and
-    LSE written once (4 B per row)."""
-    rows = w.heads * int(cu[-1]) if w.varlen else w.batch * w.heads * w.seqlen
-    return rows * (4 * w.head_dim * 2 + 4)
+    LSE written once (4 B per row); K and V have the key/value head count."""
+    tokens = int(cu[-1]) if w.varlen else w.batch * w.seqlen
+    return tokens * (w.heads * (2 * w.head_dim * 2 + 4) + w.kv_heads * 2 * w.head_dim * 2)
 
 
 def kernel_name(w, cu=None) -> str:
@@ -136,9 +137,11 @@ def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
     if w.varlen:
         cu_l = cu.tolist()
         order = [(h, s) for s in range(w.num_seqs) for h in range(w.heads)]
+        g = w.heads // w.kv_heads
         for (h, s) in order:
             a, b = cu_l[s], cu_l[s + 1]
-            qs, ks, vs = (x[h, a:b].float().numpy() for x in (q, k, v))
+            qs = q[h, a:b].float().numpy()
+            ks, vs = (x[h // g, a:b].float().numpy() for x in (k, v))
             t0 = time.perf_counter()
             oracle.attention_head(qs, ks, vs, w.softmax_scale, w.causal, w.window_left,
                                   w.window_right)
@@ -151,9 +154,11 @@ def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
         sample = f"{len(units)} (sequence, head) pairs of the packed batch, whole"
     else:
         f_head = 4.0 * w.seqlen ** 2 * w.head_dim / (2 if w.causal else 1)
+        g = w.heads // w.kv_heads
         for b in range(w.batch):
             for h in range(w.heads):
-                qs, ks, vs = (x[b, h].float().numpy() for x in (q, k, v))
+                qs = q[b, h].float().numpy()
+                ks, vs = (x[b, h // g].float().numpy() for x in (k, v))
                 t0 = time.perf_counter()
                 oracle.attention_head(qs, ks, vs, w.softmax_scale, w.causal, w.window_left,
                                       w.window_right)
@@ -222,7 +227,8 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_49_amd import (attn_fwd, attn_fwd_splitkv, attn_fwd_varlen,
+    from exact_attention_49_amd import (attn_fwd, attn_fwd_gqa, attn_fwd_splitkv,
+                                        attn_fwd_varlen, attn_fwd_varlen_gqa,
                                         splitkv_num_splits, splitkv_workspace_size)
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -250,12 +256,13 @@ def main() -> int:
                              window_right=w.window_right, out=od, lse=lsed, num_splits=0,
                              workspace=ws)
         elif w.varlen:
-            attn_fwd_varlen(qd, kd, vd, cud, max_len, causal=w.causal,
-                            window_left=w.window_left, window_right=w.window_right, out=od,
-                            lse=lsed)
+            (attn_fwd_varlen_gqa if w.heads_kv else attn_fwd_varlen)(
+                qd, kd, vd, cud, max_len, causal=w.causal, window_left=w.window_left,
+                window_right=w.window_right, out=od, lse=lsed)
         else:
-            attn_fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left,
-                     window_right=w.window_right, out=od, lse=lsed)
+            (attn_fwd_gqa if w.heads_kv else attn_fwd)(
+                qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                window_right=w.window_right, out=od, lse=lsed)
 
     for _ in range(args.warmup):
         if flush_buf is not None:
@@ -304,7 +311,8 @@ def main() -> int:
     peak = PEAK_TFLOPS[w.dtype]
     traffic = load_traffic(w.name)
 
-    config = {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim, "dtype": w.dtype,
+    config = {"workload": w.name, "heads": w.heads, "heads_kv": w.kv_heads,
+              "head_dim": w.head_dim, "dtype": w.dtype,
               "causal": w.causal, "window_left": w.window_left,
               "window_right": w.window_right, "seed": w.seed, "value_scale": w.value_scale}
     if w.varlen:
@@ -340,8 +348,8 @@ def main() -> int:
         out["cold_cache"] = cold
     if w.splitkv:  # the same problem through the plain entry point, for context
         def plain():
-            attn_fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left,
-                     window_right=w.window_right, out=od, lse=lsed)
+            attn_fwd_gqa(qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                         window_right=w.window_right, out=od, lse=lsed)
         for _ in range(3):
             plain()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -351,7 +359,7 @@ def main() -> int:
         ev1.record(stream)
         torch.cuda.synchronize()
         pm = ev0.elapsed_time(ev1) / 20
-        out["plain_path"] = {"entry_point": "attn_fwd", "avg_launch_ms": round(pm, 4),
+        out["plain_path"] = {"entry_point": "attn_fwd_gqa", "avg_launch_ms": round(pm, 4),
                              "tflops": round(flops / (pm / 1e3) / 1e12, 2)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, cu, args.cpu_budget)

@@ -2,16 +2,17 @@
 
 The compute path is a C-ABI shared library of hand-written HIP kernels
 (`exact_attention_49_amd/csrc`, declared in `include/exact_attn.h`); `attn_fwd`,
-`attn_fwd_varlen` and their split-KV variants below are thin ctypes bindings that marshal
+`attn_fwd_varlen` and their grouped-query and split-KV variants below are thin ctypes bindings that marshal
 torch device tensors and the current HIP stream into it.  The library is loaded on first use and its absence is an error.
 """
 
-from .binding import (AttnError, attn_fwd, attn_fwd_splitkv, attn_fwd_varlen,  # noqa: F401
-                      attn_fwd_varlen_splitkv, library_path, load_library, splitkv_num_splits,
+from .binding import (AttnError, attn_fwd, attn_fwd_gqa, attn_fwd_splitkv,  # noqa: F401
+                      attn_fwd_varlen, attn_fwd_varlen_gqa, attn_fwd_varlen_splitkv, library_path, load_library, splitkv_num_splits,
                       splitkv_workspace_size, varlen_splitkv_num_splits,
                       varlen_splitkv_workspace_size)
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
+           "attn_fwd_splitkv",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "library_path",
            "load_library"]

@@ -14,7 +14,8 @@ import threading
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_splitkv",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
+           "attn_fwd_splitkv",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "library_path",
            "load_library", "STATUS", "EXPORTED_SYMBOLS"]
@@ -39,10 +40,13 @@ EXPORTED_SYMBOLS = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P]),
-    "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P,
-                              _S, _P]),
-    "attn_fwd_varlen_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
-                                     _I, _I, _I, _P, _S, _P]),
+    "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "attn_fwd_varlen_gqa": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                 _I, _I, _P]),
+    "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
+                              _P, _S, _P]),
+    "attn_fwd_varlen_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                     _I, _I, _I, _I, _P, _S, _P]),
     "attn_fwd_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
@@ -104,54 +108,64 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _dense_args(q, k, v, softmax_scale, out, lse, return_lse):
+def _out_lse(q, out, lse, return_lse, lse_shape, lse_text):
+    if out is None:
+        out = torch.empty_like(q)
+    _device_tensor(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise AttnError("out must match q in shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _device_tensor(lse, "lse")
+        if tuple(lse.shape) != tuple(lse_shape) or lse.dtype != torch.float32:
+            raise AttnError(f"lse must be float32 {lse_text}")
+    return out, lse
+
+
+def _check_dtypes(q, k, v):
+    if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise AttnError("q, k, v must share one dtype: float16 or bfloat16")
+
+
+def _dense_args(q, k, v, softmax_scale, out, lse, return_lse, grouped):
+    """Checks a dense call; k, v may have fewer heads than q when `grouped`."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _device_tensor(t, n)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise AttnError("q, k, v must all be [B, H, N, d] with equal shapes")
-    if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise AttnError("q, k, v must share one dtype: float16 or bfloat16")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise AttnError("q must be [B, H, N, d] and k, v [B, Hkv, N, d] with equal shapes")
     bsz, nh, n, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (bsz, n, d):
+        raise AttnError("k, v must match q in batch, sequence length and head dim")
+    if not grouped and hkv != nh:
+        raise AttnError("k, v must have as many heads as q (attn_fwd_gqa takes fewer)")
+    _check_dtypes(q, k, v)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    _device_tensor(out, "out")
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise AttnError("out must match q in shape and dtype")
-    if lse is None and return_lse:
-        lse = torch.empty((bsz, nh, n), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _device_tensor(lse, "lse")
-        if lse.shape != (bsz, nh, n) or lse.dtype != torch.float32:
-            raise AttnError("lse must be float32 [B, H, N]")
-    return bsz, nh, n, d, float(softmax_scale), out, lse
+    out, lse = _out_lse(q, out, lse, return_lse, (bsz, nh, n), "[B, H, N]")
+    return bsz, nh, hkv, n, d, float(softmax_scale), out, lse
 
 
-def _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse, return_lse):
+def _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse, return_lse, grouped):
+    """Checks a packed call; k, v may have fewer heads than q when `grouped`."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens")):
         _device_tensor(t, n)
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise AttnError("q, k, v must all be [H, total_tokens, d] with equal shapes")
-    if q.dtype not in DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise AttnError("q, k, v must share one dtype: float16 or bfloat16")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise AttnError("q must be [H, total_tokens, d] and k, v [Hkv, total_tokens, d]")
+    nh, total, d = q.shape
+    hkv = k.shape[0]
+    if (k.shape[1], k.shape[2]) != (total, d):
+        raise AttnError("k, v must match q in total tokens and head dim")
+    if not grouped and hkv != nh:
+        raise AttnError("k, v must have as many heads as q (attn_fwd_varlen_gqa takes fewer)")
+    _check_dtypes(q, k, v)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise AttnError("cu_seqlens must be a 1-D int32 tensor of num_seqs + 1 entries")
-    nh, total, d = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    _device_tensor(out, "out")
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise AttnError("out must match q in shape and dtype")
-    if lse is None and return_lse:
-        lse = torch.empty((nh, total), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _device_tensor(lse, "lse")
-        if lse.shape != (nh, total) or lse.dtype != torch.float32:
-            raise AttnError("lse must be float32 [H, total_tokens]")
-    return nh, total, d, float(softmax_scale), out, lse
+    out, lse = _out_lse(q, out, lse, return_lse, (nh, total), "[H, total_tokens]")
+    return nh, hkv, total, d, float(softmax_scale), out, lse
 
 
 def _workspace(nbytes: int, workspace, device):
@@ -174,7 +188,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
 
     Returns (o, lse) with o like q and lse fp32 [B, H, N] (lse is None if return_lse is False
     and no lse buffer was given).  Launches on the current stream."""
-    bsz, nh, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse, return_lse)
+    bsz, nh, _, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
+                                                    return_lse, grouped=False)
     lib = load_library()
     st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
@@ -192,8 +207,8 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Packed variable-length forward.  q, k, v: [H, total, d]; cu_seqlens: int32 GPU tensor
     [num_seqs + 1]; max_seqlen: a host bound on the sequence lengths.
     Returns (o [H, total, d], lse fp32 [H, total])."""
-    nh, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse,
-                                                 return_lse)
+    nh, _, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out,
+                                                    lse, return_lse, grouped=False)
     lib = load_library()
     st = lib.attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
@@ -202,6 +217,43 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              int(bool(causal)), int(window_left), int(window_right),
                              _stream_handle(q.device))
     _check(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def attn_fwd_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                 window_left: int = -1, window_right: int = -1,
+                 softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Grouped-query dense forward: q [B, Hq, N, d], k and v [B, Hkv, N, d] with Hkv dividing
+    Hq; query head h uses key/value head h // (Hq // Hkv).  Returns (o like q, lse fp32
+    [B, Hq, N])."""
+    bsz, hq, hkv, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
+                                                      return_lse, grouped=True)
+    lib = load_library()
+    st = lib.attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, bsz, hq, hkv, n, d,
+                          DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                          int(window_left), int(window_right), _stream_handle(q.device))
+    _check(st, "attn_fwd_gqa")
+    return out, lse
+
+
+def attn_fwd_varlen_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                        window_left: int = -1, window_right: int = -1,
+                        softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Grouped-query packed forward: q [Hq, total, d], k and v [Hkv, total, d]."""
+    hq, hkv, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out,
+                                                      lse, return_lse, grouped=True)
+    lib = load_library()
+    st = lib.attn_fwd_varlen_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen),
+                                 total, hq, hkv, d, DTYPE_CODES[q.dtype], scale,
+                                 int(bool(causal)), int(window_left), int(window_right),
+                                 _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen_gqa")
     return out, lse
 
 
@@ -234,14 +286,16 @@ def attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
                      softmax_scale: float | None = None, out: torch.Tensor | None = None,
                      lse: torch.Tensor | None = None, return_lse: bool = True,
                      num_splits: int = 0, workspace: torch.Tensor | None = None):
-    """attn_fwd with the key range of every q-tile split over num_splits work items (0: the
-    library chooses) and merged.  The workspace is allocated here unless one is given."""
-    bsz, nh, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse, return_lse)
+    """attn_fwd (or attn_fwd_gqa, when k and v have fewer heads than q) with the key range of
+    every q-tile split over num_splits work items (0: the library chooses) and merged.  The
+    workspace is allocated here unless one is given."""
+    bsz, nh, hkv, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
+                                                      return_lse, grouped=True)
     lib = load_library()
     nbytes = lib.attn_fwd_splitkv_workspace_size(bsz, nh, n, d, int(num_splits))
     ws = _workspace(nbytes, workspace, q.device)
     st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr() if lse is not None else None, bsz, nh, n, d,
+                              lse.data_ptr() if lse is not None else None, bsz, nh, hkv, n, d,
                               DTYPE_CODES[q.dtype], scale, int(bool(causal)),
                               int(window_left), int(window_right), int(num_splits),
                               ws.data_ptr() if ws is not None else None,
@@ -258,9 +312,9 @@ def attn_fwd_varlen_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                             return_lse: bool = True, num_splits: int = 0,
                             workspace: torch.Tensor | None = None):
-    """attn_fwd_varlen with split-KV (see attn_fwd_splitkv)."""
-    nh, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out, lse,
-                                                 return_lse)
+    """attn_fwd_varlen (or attn_fwd_varlen_gqa) with split-KV (see attn_fwd_splitkv)."""
+    nh, hkv, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out,
+                                                      lse, return_lse, grouped=True)
     lib = load_library()
     ns = cu_seqlens.numel() - 1
     nbytes = lib.attn_fwd_varlen_splitkv_workspace_size(ns, int(max_seqlen), total, nh, d,
@@ -268,8 +322,8 @@ def attn_fwd_varlen_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ws = _workspace(nbytes, workspace, q.device)
     st = lib.attn_fwd_varlen_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      lse.data_ptr() if lse is not None else None,
-                                     cu_seqlens.data_ptr(), ns, int(max_seqlen), total, nh, d,
-                                     DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                                     cu_seqlens.data_ptr(), ns, int(max_seqlen), total, nh,
+                                     hkv, d, DTYPE_CODES[q.dtype], scale, int(bool(causal)),
                                      int(window_left), int(window_right), int(num_splits),
                                      ws.data_ptr() if ws is not None else None,
                                      ws.numel() * ws.element_size() if ws is not None else 0,

@@ -138,10 +138,14 @@ struct Plan {
 
 // shape: 1 = choose (big if the grid is large enough), 0 = small shape.
 Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
-                int heads, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
-                int window_left, int window_right, int shape) {
+                int heads, int heads_kv, int seqlen, int head_dim, int dtype,
+                float softmax_scale, int causal, int window_left, int window_right, int shape) {
   Plan p;
   if (batch < 0 || heads < 0 || seqlen < 0) { p.status = ATTN_ERR_INVALID_ARG; return p; }
+  if (heads > 0 && (heads_kv < 1 || heads % heads_kv != 0)) {
+    p.status = ATTN_ERR_INVALID_ARG;
+    return p;
+  }
   p.rows = (long)batch * heads * seqlen;
   if (p.rows == 0) {  // empty problem: still reject malformed non-size arguments
     if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16)
@@ -176,6 +180,8 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   a.scale_log2 = softmax_scale * kLog2e;
   a.window_left = wl;
   a.window_right = wr;
+  a.heads_q = heads;
+  a.kv_group = heads / heads_kv;
   a.num_splits = 1;
   p.n_work = (long)batch * heads * a.tiles_per_head;
   p.max_len = seqlen;
@@ -184,10 +190,14 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
 
 Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                  const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
-                 int heads, int head_dim, int dtype, float softmax_scale, int causal,
-                 int window_left, int window_right, int shape) {
+                 int heads, int heads_kv, int head_dim, int dtype, float softmax_scale,
+                 int causal, int window_left, int window_right, int shape) {
   Plan p;
   if (num_seqs < 0 || total_tokens < 0 || heads < 0 || max_seqlen < 0) {
+    p.status = ATTN_ERR_INVALID_ARG;
+    return p;
+  }
+  if (heads > 0 && (heads_kv < 1 || heads % heads_kv != 0)) {
     p.status = ATTN_ERR_INVALID_ARG;
     return p;
   }
@@ -235,6 +245,8 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
   a.scale_log2 = softmax_scale * kLog2e;
   a.window_left = wl;
   a.window_right = wr;
+  a.heads_q = heads;
+  a.kv_group = heads / heads_kv;
   a.num_splits = 1;
   p.n_work = (long)heads * slots;
   p.max_len = max_seqlen;
@@ -293,8 +305,8 @@ extern "C" {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
              int heads, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
              int window_left, int window_right, void* stream) {
-  Plan p = plan_dense(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
-                      causal, window_left, window_right, 1);
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads, heads, seqlen, head_dim, dtype,
+                      softmax_scale, causal, window_left, window_right, 1);
   if (p.status != ATTN_OK || p.empty) return p.status;
   return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
 }
@@ -304,7 +316,30 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     int heads, int head_dim, int dtype, float softmax_scale, int causal,
                     int window_left, int window_right, void* stream) {
   Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, heads,
-                       head_dim, dtype, softmax_scale, causal, window_left, window_right, 1);
+                       heads, head_dim, dtype, softmax_scale, causal, window_left, window_right,
+                       1);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads_q, int heads_kv, int seqlen, int head_dim, int dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream) {
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen, head_dim, dtype,
+                      softmax_scale, causal, window_left, window_right, 1);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
+}
+
+int attn_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                        int total_tokens, int heads_q, int heads_kv, int head_dim, int dtype,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        void* stream) {
+  Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
+                       heads_q, heads_kv, head_dim, dtype, softmax_scale, causal, window_left,
+                       window_right, 1);
   if (p.status != ATTN_OK || p.empty) return p.status;
   return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
 }
@@ -327,17 +362,17 @@ size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int hea
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int batch, int heads, int seqlen, int head_dim, int dtype,
+                     int batch, int heads, int heads_kv, int seqlen, int head_dim, int dtype,
                      float softmax_scale, int causal, int window_left, int window_right,
                      int num_splits, void* workspace, size_t workspace_size, void* stream) {
   if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
-  Plan p = plan_dense(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
-                      causal, window_left, window_right, 0);
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
+                      softmax_scale, causal, window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
   const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
   if (s == 1)
-    return attn_fwd(q, k, v, o, lse, batch, heads, seqlen, head_dim, dtype, softmax_scale,
-                    causal, window_left, window_right, stream);
+    return attn_fwd_gqa(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
+                        softmax_scale, causal, window_left, window_right, stream);
   return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 
@@ -366,19 +401,20 @@ size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int 
 
 int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                             const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
-                            int total_tokens, int heads, int head_dim, int dtype,
-                            float softmax_scale, int causal, int window_left, int window_right,
-                            int num_splits, void* workspace, size_t workspace_size,
-                            void* stream) {
+                            int total_tokens, int heads, int heads_kv, int head_dim,
+                            int dtype, float softmax_scale, int causal, int window_left,
+                            int window_right, int num_splits, void* workspace,
+                            size_t workspace_size, void* stream) {
   if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
   Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens, heads,
-                       head_dim, dtype, softmax_scale, causal, window_left, window_right, 0);
+                       heads_kv, head_dim, dtype, softmax_scale, causal, window_left,
+                       window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
   const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
   if (s == 1)
-    return attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
-                           heads, head_dim, dtype, softmax_scale, causal, window_left,
-                           window_right, stream);
+    return attn_fwd_varlen_gqa(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen,
+                               total_tokens, heads, heads_kv, head_dim, dtype, softmax_scale,
+                               causal, window_left, window_right, stream);
   return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 

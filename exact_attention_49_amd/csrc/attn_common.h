@@ -60,6 +60,11 @@ struct FwdArgs {
   float scale_log2;           // softmax_scale * log2(e): scores are exponentiated base 2
   int window_left;            // -1 = unbounded (MASK_WINDOW only)
   int window_right;           // -1 = unbounded (MASK_WINDOW only; causal folded in as 0)
+  // grouped-query attention: q/o have heads_q heads, k/v heads_q / kv_group; query head h
+  // reads key/value head h / kv_group (kv_group = 1: one K/V head per query head; page
+  // "mainloop_bwd_sm90_tma_gmma_ws.hpp", qhead_per_khead division)
+  int heads_q;
+  int kv_group;
   // split-KV mode only: the key tiles of each q-tile are shared out among num_splits work
   // items, which write normalised fp32 partial outputs and their LSE instead of o / lse
   int num_splits;             // 1 outside split-KV mode
@@ -219,7 +224,8 @@ template <int D> __device__ __forceinline__ int swz_v(int r) {
 struct Work {
   int tile;    // q-tile index within the sequence
   int seqlen;  // rows (= keys) of the sequence
-  long row0;   // index of the sequence's token 0 in the [*, D] row space of q/k/v/o and lse
+  long row0;   // index of the sequence's token 0 in the [*, D] row space of q/o and lse
+  long kv_row0;  // the same for k/v (differs from row0 with grouped K/V heads)
   int split;   // split-KV: which share of the q-tile's key tiles (0 otherwise)
 };
 
@@ -242,6 +248,10 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
     w.tile = (MODE != MASK_NONE) ? per - 1 - t : t;
     w.seqlen = a.seqlen;
     w.row0 = (long)bh * a.seqlen;
+    // (batch, query head) -> (batch, K/V head); query heads of a group are neighbours, so
+    // they run on the same XCD and share its L2 copy of the K/V head
+    const int b = bh / a.heads_q, h = bh - b * a.heads_q;
+    w.kv_row0 = ((long)b * (a.heads_q / a.kv_group) + h / a.kv_group) * a.seqlen;
     return true;
   }
   const int h = wid / per;
@@ -257,6 +267,7 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
       w.tile = (MODE != MASK_NONE) ? nt - 1 - t : t;
       w.seqlen = c_next - c_prev;
       w.row0 = (long)h * a.total_tokens + c_prev;
+      w.kv_row0 = (long)(h / a.kv_group) * a.total_tokens + c_prev;
       return true;
     }
     acc += nt;

@@ -61,8 +61,8 @@ void attn_fwd_kernel(FwdArgs a) {
   if (wl >= 0) kw_lo = max(0, qw0 - wl);
   if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
 
-  const uint16_t* __restrict__ kp = a.k + w.row0 * D;
-  const uint16_t* __restrict__ vp = a.v + w.row0 * D;
+  const uint16_t* __restrict__ kp = a.k + w.kv_row0 * D;
+  const uint16_t* __restrict__ vp = a.v + w.kv_row0 * D;
   const int qrow = qw0 + l32;
 
   i32x4 qf[D / 16];

@@ -6,8 +6,9 @@ rounded to the I/O dtype, so they see identical inputs.
 
 Recipe: a CPU `torch.Generator` seeded with the workload's seed draws, in this order,
 (for packed batches) the sequence lengths with `randint`, then Q, K and V with `randn` in
-float32; Q, K and V are multiplied by the workload's value scale (an exact power of two) and
-cast to the I/O dtype with round-to-nearest-even.
+float32 (K and V with the key/value head count, which is below Q's for grouped-query
+problems); Q, K and V are multiplied by the workload's value scale (an exact power of two)
+and cast to the I/O dtype with round-to-nearest-even.
 """
 
 from __future__ import annotations
@@ -44,12 +45,17 @@ class Workload:
     window_left: int = -1
     window_right: int = -1
     value_scale: float = 1.0
+    heads_kv: int = 0       # key/value heads (grouped-query attention); 0: as many as `heads`
     splitkv: bool = False   # run through the split-KV entry point
     note: str = field(default="", compare=False)
 
     @property
     def varlen(self) -> bool:
         return self.num_seqs > 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.heads_kv or self.heads
 
     @property
     def softmax_scale(self) -> float:
@@ -84,14 +90,19 @@ WORKLOADS = {
         Workload("splitkv_bf16_d128_h2_n16384", batch=1, heads=2, seqlen=16384,
                  head_dim=128, dtype="bf16", causal=True, seed=4906, splitkv=True,
                  note="B=1 H=2 N=16384 d=128 bf16 causal, split-KV (low occupancy)"),
+        # grouped-query attention: 32 query heads on 8 key/value heads (groups of 4)
+        Workload("gqa_bf16_d128_hq32_hkv8_n8192", batch=2, heads=32, heads_kv=8,
+                 seqlen=8192, head_dim=128, dtype="bf16", causal=True, seed=4907,
+                 value_scale=0.5,
+                 note="B=2 Hq=32 Hkv=8 N=8192 d=128 bf16 causal, inputs N(0,1)*0.5"),
     ]
 }
 
 
-def _randn_qkv(gen: torch.Generator, shape, dtype: torch.dtype, value_scale: float):
+def _randn_qkv(gen: torch.Generator, shape, kv_shape, dtype: torch.dtype, value_scale: float):
     out = []
-    for _ in range(3):
-        x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    for sh in (shape, kv_shape, kv_shape):
+        x = torch.randn(sh, generator=gen, dtype=torch.float32)
         if value_scale != 1.0:
             x = x * value_scale
         out.append(x.to(dtype))
@@ -99,15 +110,19 @@ def _randn_qkv(gen: torch.Generator, shape, dtype: torch.dtype, value_scale: flo
 
 
 def make_dense(batch: int, heads: int, seqlen: int, head_dim: int, dtype: str, seed: int,
-               value_scale: float = 1.0):
-    """Q, K, V as contiguous CPU tensors [B, H, N, d] in the I/O dtype."""
+               value_scale: float = 1.0, heads_kv: int = 0):
+    """Q [B, H, N, d] and K, V [B, Hkv, N, d] (Hkv = heads_kv, or H when 0) as contiguous CPU
+    tensors in the I/O dtype."""
     gen = torch.Generator("cpu").manual_seed(seed)
-    return _randn_qkv(gen, (batch, heads, seqlen, head_dim), _DTYPES[dtype], value_scale)
+    return _randn_qkv(gen, (batch, heads, seqlen, head_dim),
+                      (batch, heads_kv or heads, seqlen, head_dim), _DTYPES[dtype], value_scale)
 
 
 def make_varlen(num_seqs: int, min_len: int, max_len: int, heads: int, head_dim: int,
-                dtype: str, seed: int, value_scale: float = 1.0, lengths=None):
-    """Q, K, V as contiguous CPU tensors [H, total, d] plus int32 cu_seqlens [num_seqs + 1].
+                dtype: str, seed: int, value_scale: float = 1.0, lengths=None,
+                heads_kv: int = 0):
+    """Q [H, total, d] and K, V [Hkv, total, d] as contiguous CPU tensors plus int32
+    cu_seqlens [num_seqs + 1].
 
     Lengths are drawn uniformly from [min_len, max_len] unless `lengths` is given."""
     gen = torch.Generator("cpu").manual_seed(seed)
@@ -118,7 +133,8 @@ def make_varlen(num_seqs: int, min_len: int, max_len: int, heads: int, head_dim:
     cu = torch.zeros(lens.numel() + 1, dtype=torch.int64)
     cu[1:] = torch.cumsum(lens, 0)
     total = int(cu[-1])
-    q, k, v = _randn_qkv(gen, (heads, total, head_dim), _DTYPES[dtype], value_scale)
+    q, k, v = _randn_qkv(gen, (heads, total, head_dim), (heads_kv or heads, total, head_dim),
+                         _DTYPES[dtype], value_scale)
     return q, k, v, cu.to(torch.int32)
 
 
@@ -126,5 +142,6 @@ def make_workload(w: Workload):
     """Tensors for a named workload: (q, k, v) dense or (q, k, v, cu_seqlens) packed."""
     if w.varlen:
         return make_varlen(w.num_seqs, w.min_len, w.max_len, w.heads, w.head_dim, w.dtype,
-                           w.seed, w.value_scale)
-    return make_dense(w.batch, w.heads, w.seqlen, w.head_dim, w.dtype, w.seed, w.value_scale)
+                           w.seed, w.value_scale, heads_kv=w.heads_kv)
+    return make_dense(w.batch, w.heads, w.seqlen, w.head_dim, w.dtype, w.seed, w.value_scale,
+                      heads_kv=w.heads_kv)

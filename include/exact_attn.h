@@ -92,6 +92,30 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     int causal, int window_left, int window_right, void* stream);
 
 /*
+ * Grouped-query variants (GQA; MQA when heads_kv = 1): q, o and lse have heads_q heads, k and
+ * v have heads_kv heads, heads_kv >= 1 divides heads_q, and query head h attends with key /
+ * value head h / (heads_q / heads_kv) (page "mainloop_bwd_sm90_tma_gmma_ws.hpp", the
+ * qhead_per_khead division: a query head's key/value head is its index divided by the number
+ * of query heads per key/value head).
+ *   attn_fwd_gqa        : q, o [batch, heads_q, seqlen, head_dim];
+ *                         k, v [batch, heads_kv, seqlen, head_dim]; lse [batch, heads_q, seqlen]
+ *   attn_fwd_varlen_gqa : q, o [heads_q, total_tokens, head_dim];
+ *                         k, v [heads_kv, total_tokens, head_dim]; lse [heads_q, total_tokens]
+ * A heads_kv that is < 1 or does not divide heads_q gives ATTN_ERR_INVALID_ARG.  Everything
+ * else is as for attn_fwd / attn_fwd_varlen, which are the heads_kv = heads_q case.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int batch, int heads_q, int heads_kv, int seqlen, int head_dim, int dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream);
+
+int attn_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                        int total_tokens, int heads_q, int heads_kv, int head_dim, int dtype,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        void* stream);
+
+/*
  * Split-KV variants, for problems whose plain grid cannot fill the GPU (few heads and q-tiles
  * over long sequences).  The key tiles that every q-tile sees are shared out among num_splits
  * work items; each writes a normalised fp32 partial output O_s and the natural-log LSE_s of
@@ -109,22 +133,25 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  *                    num_splits; otherwise ATTN_ERR_INVALID_ARG.  Its contents on entry do not
  *                    matter and on exit are unspecified; two calls in flight at once must not
  *                    share a workspace.
- * All other arguments, layouts and errors are those of attn_fwd / attn_fwd_varlen.
+ *   heads, heads_kv: query heads and key/value heads, as heads_q and heads_kv of the
+ *                    grouped-query variants (heads_kv = heads is plain multi-head attention).
+ * All other arguments, layouts and errors are those of attn_fwd_gqa / attn_fwd_varlen_gqa.
+ * The workspace depends on the query heads only.
  */
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int batch, int heads, int seqlen, int head_dim, int dtype,
+                     int batch, int heads, int heads_kv, int seqlen, int head_dim, int dtype,
                      float softmax_scale, int causal, int window_left, int window_right,
                      int num_splits, void* workspace, size_t workspace_size, void* stream);
 
 int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                             const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
-                            int total_tokens, int heads, int head_dim, int dtype,
-                            float softmax_scale, int causal, int window_left, int window_right,
-                            int num_splits, void* workspace, size_t workspace_size,
-                            void* stream);
+                            int total_tokens, int heads, int heads_kv, int head_dim,
+                            int dtype, float softmax_scale, int causal, int window_left,
+                            int window_right, int num_splits, void* workspace,
+                            size_t workspace_size, void* stream);
 
-/* Workspace bytes the split-KV calls need for these sizes and num_splits (0 = the count the
- * library would choose).  0 when no workspace is needed (one split) or the arguments are
+/* Workspace bytes the split-KV calls need for these sizes (heads = query heads) and
+ * num_splits (0 = the count the library would choose).  0 when no workspace is needed (one split) or the arguments are
  * invalid.  Host-only: no device is touched. */
 size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
                                        int num_splits);

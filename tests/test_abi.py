@@ -44,6 +44,36 @@ def test_library_exports_every_header_function(lib):
         assert isinstance(getattr(lib, fn), ctypes._CFuncPtr)
 
 
+_CTYPE_OF = {"int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t}
+
+
+def header_signatures():
+    """{name: (return type, [argument types])} parsed from the header, as ctypes types."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    sigs = {}
+    for ret, name, params in re.findall(r"^([A-Za-z_][\w \*]*?)\s*\b(attn_\w+)\s*\(([^)]*)\)\s*;",
+                                        text, flags=re.M):
+        def ctype(decl):
+            decl = decl.strip()
+            if decl == "void" or not decl:
+                return None
+            if "*" in decl:
+                return ctypes.c_char_p if decl.startswith("const char") else ctypes.c_void_p
+            return _CTYPE_OF[decl.rsplit(None, 1)[0].replace("const ", "")]
+        args = [ctype(p) for p in params.split(",")]
+        sigs[name] = (ctype(ret + " x" if "*" not in ret else ret), [a for a in args if a])
+    return sigs
+
+
+def test_binding_signatures_match_the_header():
+    sigs = header_signatures()
+    assert set(sigs) == set(header_functions())
+    for name, (ret, args) in sigs.items():
+        b_ret, b_args = binding.EXPORTED_SYMBOLS[name]
+        assert b_ret == ret, name
+        assert b_args == args, name
+
+
 def test_status_strings(lib):
     for code, name in binding.STATUS.items():
         assert lib.attn_status_string(code).decode().startswith(name)
@@ -113,11 +143,12 @@ def test_binding_refuses_cpu_tensors():
 # ---- split-KV entry points (host-side validation and workspace sizing only) ----------------
 
 def call_dense_split(lib, ns=2, ws=A, wsb=1 << 30, **kw):
-    args = dict(q=A, k=A, v=A, o=A, lse=None, b=1, h=1, n=4096, d=128, dtype=1, scale=SCALE,
-                causal=0, wl=-1, wr=-1)
+    args = dict(q=A, k=A, v=A, o=A, lse=None, b=1, h=1, hkv=None, n=4096, d=128, dtype=1,
+                scale=SCALE, causal=0, wl=-1, wr=-1)
     args.update(kw)
+    hkv = args["h"] if args["hkv"] is None else args["hkv"]
     return lib.attn_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"],
-                                args["b"], args["h"], args["n"], args["d"], args["dtype"],
+                                args["b"], args["h"], hkv, args["n"], args["d"], args["dtype"],
                                 args["scale"], args["causal"], args["wl"], args["wr"], ns, ws,
                                 wsb, None)
 
@@ -154,6 +185,7 @@ def test_splitkv_automatic_count(lib):
     (dict(ns=-1), 1), (dict(ns=65), 1),                      # split count
     (dict(ws=None), 1), (dict(ws=A + 64), 1), (dict(wsb=1024), 1),   # workspace
     (dict(q=None), 1), (dict(d=96), 2), (dict(dtype=5), 3), (dict(o=A + 2), 4),
+    (dict(h=8, hkv=3), 1), (dict(h=8, hkv=0), 1), (dict(h=4, hkv=8), 1),   # head grouping
 ])
 def test_splitkv_rejects_bad_arguments(lib, kw, status):
     assert call_dense_split(lib, **kw) == status
@@ -163,3 +195,52 @@ def test_splitkv_one_split_needs_no_workspace(lib):
     # with one split the plain kernels run; validation still happens on the host first
     assert call_dense_split(lib, ns=1, ws=None, wsb=0, d=96) == 2
     assert call_dense_split(lib, ns=0, ws=None, wsb=0, b=0) == 0   # empty problem
+
+
+# ---- grouped-query entry points (host-side validation only) ----------------------------------
+
+def call_gqa(lib, hq=8, hkv=2, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=None, b=1, n=16, d=64, dtype=1, scale=SCALE, causal=0,
+                wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_fwd_gqa(args["q"], args["k"], args["v"], args["o"], args["lse"], args["b"],
+                            hq, hkv, args["n"], args["d"], args["dtype"], args["scale"],
+                            args["causal"], args["wl"], args["wr"], None)
+
+
+def call_varlen_gqa(lib, hq=8, hkv=2, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=None, cu=A, ns=2, maxs=8, total=16, d=64, dtype=1,
+                scale=SCALE, causal=0, wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_fwd_varlen_gqa(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                   args["cu"], args["ns"], args["maxs"], args["total"], hq, hkv,
+                                   args["d"], args["dtype"], args["scale"], args["causal"],
+                                   args["wl"], args["wr"], None)
+
+
+@pytest.mark.parametrize("call", [call_gqa, call_varlen_gqa])
+@pytest.mark.parametrize("hq,hkv", [(8, 3), (8, 0), (8, -2), (4, 8), (6, 4)])
+def test_gqa_rejects_head_counts_that_do_not_divide(lib, call, hq, hkv):
+    assert call(lib, hq=hq, hkv=hkv) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(d=96), 2), (dict(dtype=4), 3), (dict(k=A + 2), 4),
+    (dict(causal=3), 1),
+])
+def test_gqa_other_checks_match_the_plain_calls(lib, kw, status):
+    assert call_gqa(lib, **kw) == status
+    assert call_varlen_gqa(lib, **kw) == status
+
+
+def test_gqa_empty_problem_is_a_no_op(lib):
+    assert call_gqa(lib, hq=0, hkv=1, q=None, k=None, v=None, o=None) == 0
+    assert call_gqa(lib, b=0, q=None, k=None, v=None, o=None) == 0
+    assert call_varlen_gqa(lib, ns=0, q=None, k=None, v=None, o=None, cu=None) == 0
+
+
+def test_binding_gqa_checks_shapes():
+    import torch
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(binding.AttnError, match="GPU tensor"):
+        binding.attn_fwd_gqa(q, q[:, :2], q[:, :2])
