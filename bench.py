@@ -4,7 +4,8 @@
 
 One step = one forward pass (one attn_fwd / attn_fwd_varlen call, attn_fwd_gqa for the
 grouped-query workload; for the split-KV workload one attn_fwd_splitkv call, which runs the
-split sweep and the merge) over the workload's
+split sweep and the merge; for the backward workload one attn_bwd call, its two kernels, with
+the forward's O and LSE computed before timing) over the workload's
 inputs, which are resident in HBM before timing starts.  W untimed steps, then exactly K timed
 steps between two device synchronisations.  Rank 0 prints one JSON line:
 
@@ -23,6 +24,7 @@ plain device copy of known size (for scaling HBM counters).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -35,19 +37,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d, halved if causal) and % of MFMA peak"
+METRIC_BWD = ("attention bwd TFLOP/s (2.5·4·B·H·N²·d, halved if causal) and % of MFMA peak")
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}    # MI355X dense MFMA, AMD's published figure
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_bf16_d128_n8192"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources: recorded HBM counters are only valid for the kernel they
-    were taken on."""
+def kernel_source_hash(backward: bool = False) -> str:
+    """Hash of the HIP sources of the forward (or the backward) kernels and the shared host
+    code: recorded HBM counters are only valid for the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_49_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip")):
+        shared = f in ("attn_common.h", "attn_api.hip")
+        if f.endswith((".h", ".hip")) and (shared or f.startswith("attn_bwd") == backward):
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -68,6 +72,10 @@ def visible_pairs(n: int, causal: bool, wl: int, wr: int) -> int:
 
 
 def workload_flops(w, cu=None) -> float:
+    """Forward: 4*B*H*N^2*d, halved when causal (packed: 4*H*d*visible pairs).  Backward: 2.5
+    times that (five N x N x d products against the forward's two)."""
+    if w.backward:
+        return 2.5 * workload_flops(dataclasses.replace(w, backward=False), cu)
     if w.varlen:
         lens = (cu[1:] - cu[:-1]).tolist()
         pairs = sum(visible_pairs(int(n), w.causal, w.window_left, w.window_right) for n in lens)
@@ -78,8 +86,11 @@ def workload_flops(w, cu=None) -> float:
 
 def workload_bytes(w, cu=None) -> float:
     """Algorithmic HBM bytes per launch: Q, K, V read once, O written once (2 B each) and
-    LSE written once (4 B per row); K and V have the key/value head count."""
+    LSE written once (4 B per row); K and V have the key/value head count.  Backward: Q, K, V,
+    O, dO read, dQ, dK, dV written (2 B each), LSE read, dPsum written and read (4 B each)."""
     tokens = int(cu[-1]) if w.varlen else w.batch * w.seqlen
+    if w.backward:
+        return tokens * (w.heads * (4 * w.head_dim * 2 + 12) + w.kv_heads * 4 * w.head_dim * 2)
     return tokens * (w.heads * (2 * w.head_dim * 2 + 4) + w.kv_heads * 2 * w.head_dim * 2)
 
 
@@ -87,6 +98,8 @@ def kernel_name(w, cu=None) -> str:
     """The kernel the library launches for a workload (mirrors the host dispatch: the wide
     kernel for d >= 256, the generic kernel for d = 64, and for d = 128 the ping-pong kernel
     once the grid of 256-row tiles has at least 1024 workgroups, else the generic one)."""
+    if w.backward:
+        return "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel (one step)"
     if w.splitkv:  # one step = the split sweep and the merge
         base = "attn_fwd_wide_kernel" if w.head_dim >= 256 else "attn_fwd_kernel"
         return f"{base} (split-KV) + attn_merge_kernel"
@@ -101,11 +114,11 @@ def kernel_name(w, cu=None) -> str:
     return "attn_fwd_pp_kernel" if tiles >= 1024 else "attn_fwd_kernel"
 
 
-def load_traffic(workload: str):
+def load_traffic(w):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE,
     scaled by a plain copy's readings), if they were taken on the current kernel sources;
     else None.  The summary holds `key: value` lines."""
-    path = os.path.join(TRAFFIC_DIR, f"attn_fwd_{workload}_hbm_traffic.txt")
+    path = os.path.join(TRAFFIC_DIR, f"{w.name}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -114,7 +127,7 @@ def load_traffic(workload: str):
             key, sep, val = line.partition(":")
             if sep:
                 rec[key.strip()] = val.strip()
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(w.backward):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -152,6 +165,26 @@ def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
             if t_total >= budget_s:
                 break
         sample = f"{len(units)} (sequence, head) pairs of the packed batch, whole"
+    elif w.backward:
+        f_head = 10.0 * w.seqlen ** 2 * w.head_dim / (2 if w.causal else 1)
+        g = w.heads // w.kv_heads
+        do = inputs_upstream(w, q)
+        for b in range(w.batch):
+            for h in range(w.heads):
+                qs, dos = q[b, h].float().numpy(), do[b, h].float().numpy()
+                ks, vs = (x[b, h // g].float().numpy() for x in (k, v))
+                t0 = time.perf_counter()
+                oracle.attention_head_backward(qs, ks, vs, dos, w.softmax_scale, w.causal,
+                                               w.window_left, w.window_right)
+                t_total += time.perf_counter() - t0
+                done_flops += f_head
+                units.append((b, h))
+                if t_total >= budget_s:
+                    break
+            if t_total >= budget_s:
+                break
+        sample = (f"{len(units)} of {w.batch * w.heads} (batch, head) pairs, whole backward "
+                  f"(N={w.seqlen}, d={w.head_dim}), fp64 numpy")
     else:
         f_head = 4.0 * w.seqlen ** 2 * w.head_dim / (2 if w.causal else 1)
         g = w.heads // w.kv_heads
@@ -182,6 +215,12 @@ def cpu_baseline(w, q, k, v, cu, budget_s: float = 20.0):
     return {"value": done_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": sample, "seconds": round(t_total, 2),
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model}
+
+
+def inputs_upstream(w, q):
+    """The workload's upstream gradient dO (a seeded draw, like the inputs)."""
+    from exact_attention_49_amd import inputs
+    return inputs.make_upstream(q.shape, w.dtype, seed=w.seed + 100, value_scale=w.value_scale)
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -227,7 +266,7 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_49_amd import (attn_fwd, attn_fwd_gqa, attn_fwd_splitkv,
+    from exact_attention_49_amd import (attn_bwd, attn_fwd, attn_fwd_gqa, attn_fwd_splitkv,
                                         attn_fwd_varlen, attn_fwd_varlen_gqa,
                                         splitkv_num_splits, splitkv_workspace_size)
     w = inputs.WORKLOADS[args.workload]
@@ -249,9 +288,18 @@ def main() -> int:
     if w.splitkv:  # caller-owned workspace, allocated before any timing
         nbytes = splitkv_workspace_size(w.batch, w.heads, w.seqlen, w.head_dim, 0)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if w.backward:  # the forward's outputs, dO, gradient buffers and workspace, before timing
+        attn_fwd_gqa(qd, kd, vd, causal=w.causal, window_left=w.window_left,
+                     window_right=w.window_right, out=od, lse=lsed)
+        dod = inputs_upstream(w, q).to(dev)
+        dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(od.numel() // w.head_dim * 4 + 256, dtype=torch.uint8, device=dev)
 
     def step():
-        if w.splitkv:
+        if w.backward:
+            attn_bwd(qd, kd, vd, od, lsed, dod, causal=w.causal, window_left=w.window_left,
+                     window_right=w.window_right, dq=dqd, dk=dkd, dv=dvd, workspace=ws)
+        elif w.splitkv:
             attn_fwd_splitkv(qd, kd, vd, causal=w.causal, window_left=w.window_left,
                              window_right=w.window_right, out=od, lse=lsed, num_splits=0,
                              workspace=ws)
@@ -309,7 +357,7 @@ def main() -> int:
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w)
 
     config = {"workload": w.name, "heads": w.heads, "heads_kv": w.kv_heads,
               "head_dim": w.head_dim, "dtype": w.dtype,
@@ -323,11 +371,14 @@ def main() -> int:
                                                 for n in lens))
     else:
         config.update(batch=w.batch, seqlen=w.seqlen)
+    if w.backward:
+        config.update(entry_point="attn_bwd", direction="backward (dQ, dK, dV)",
+                      flops_counted="2.5 x forward (five N x N x d products)")
     if w.splitkv:
         config.update(entry_point="attn_fwd_splitkv",
                       num_splits=splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim))
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_BWD if w.backward else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs, no dataset)", "config": config,
@@ -342,7 +393,7 @@ def main() -> int:
                      "min_launch_ms": round(min_launch_ms, 4),
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(w.backward),
     }
     if cold is not None:
         out["cold_cache"] = cold

@@ -17,7 +17,8 @@ import torch
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
            "attn_fwd_splitkv",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
-           "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "library_path",
+           "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "attn_bwd",
+           "attn_bwd_varlen", "library_path",
            "load_library", "STATUS", "EXPORTED_SYMBOLS"]
 
 LIB_NAME = "libexact_attn.so"
@@ -51,6 +52,10 @@ EXPORTED_SYMBOLS = {
     "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P] * 9 + [_I] * 6 + [_F] + [_I] * 3 + [_P, _S, _P]),
+    "attn_bwd_varlen": (_I, [_P] * 10 + [_I] * 7 + [_F] + [_I] * 3 + [_P, _S, _P]),
+    "attn_bwd_workspace_size": (_S, [_I, _I, _I]),
+    "attn_bwd_varlen_workspace_size": (_S, [_I, _I]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -330,3 +335,72 @@ def attn_fwd_varlen_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                      _stream_handle(q.device))
     _check(st, "attn_fwd_varlen_splitkv")
     return out, lse
+
+
+def _grad_outputs(q, k, v, dq, dk, dv):
+    out = []
+    for g, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if g is None:
+            g = torch.empty_like(like)
+        _device_tensor(g, name)
+        if g.shape != like.shape or g.dtype != like.dtype:
+            raise AttnError(f"{name} must match its input in shape and dtype")
+        out.append(g)
+    return out
+
+
+def _check_like(x, ref, name, dtype=None):
+    _device_tensor(x, name)
+    if x.shape != ref.shape or x.dtype != (dtype or ref.dtype):
+        raise AttnError(f"{name} has the wrong shape or dtype")
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
+             window_left: int = -1, window_right: int = -1,
+             softmax_scale: float | None = None, dq: torch.Tensor | None = None,
+             dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None):
+    """Backward of attn_fwd / attn_fwd_gqa: q, o, dout [B, Hq, N, d]; k, v [B, Hkv, N, d];
+    lse fp32 [B, Hq, N] (the forward's).  Returns (dq, dk, dv), allocated here unless given.
+    head_dim 64 or 128.  Launches on the current stream."""
+    bsz, hq, hkv, n, d, scale, o, lse = _dense_args(q, k, v, softmax_scale, o, lse, True,
+                                                    grouped=True)
+    _check_like(dout, q, "dout")
+    dq, dk, dv = _grad_outputs(q, k, v, dq, dk, dv)
+    lib = load_library()
+    ws = _workspace(lib.attn_bwd_workspace_size(bsz, hq, n), workspace, q.device)
+    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), bsz, hq, hkv,
+                      n, d, DTYPE_CODES[q.dtype], scale, int(bool(causal)), int(window_left),
+                      int(window_right), ws.data_ptr() if ws is not None else None,
+                      ws.numel() * ws.element_size() if ws is not None else 0,
+                      _stream_handle(q.device))
+    _check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor,
+                    max_seqlen: int, causal: bool = False, window_left: int = -1,
+                    window_right: int = -1, softmax_scale: float | None = None,
+                    dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                    dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Backward of the packed forward: q, o, dout [Hq, total, d]; k, v [Hkv, total, d]; lse fp32
+    [Hq, total].  Returns (dq, dk, dv)."""
+    hq, hkv, total, d, scale, o, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, o, lse,
+                                                    True, grouped=True)
+    _check_like(dout, q, "dout")
+    dq, dk, dv = _grad_outputs(q, k, v, dq, dk, dv)
+    lib = load_library()
+    ws = _workspace(lib.attn_bwd_varlen_workspace_size(total, hq), workspace, q.device)
+    st = lib.attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                             int(max_seqlen), total, hq, hkv, d, DTYPE_CODES[q.dtype], scale,
+                             int(bool(causal)), int(window_left), int(window_right),
+                             ws.data_ptr() if ws is not None else None,
+                             ws.numel() * ws.element_size() if ws is not None else 0,
+                             _stream_handle(q.device))
+    _check(st, "attn_bwd_varlen")
+    return dq, dk, dv

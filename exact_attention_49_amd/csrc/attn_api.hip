@@ -6,6 +6,7 @@
 #include <limits>
 
 #include "exact_attn.h"
+#include "attn_bwd.h"
 #include "attn_dispatch.h"
 
 namespace xattn {
@@ -21,6 +22,8 @@ template <> hipError_t launch_merge<64>(const MergeArgs&, bool, hipStream_t);
 template <> hipError_t launch_merge<128>(const MergeArgs&, bool, hipStream_t);
 template <> hipError_t launch_merge<256>(const MergeArgs&, bool, hipStream_t);
 template <> hipError_t launch_merge<512>(const MergeArgs&, bool, hipStream_t);
+template <> hipError_t launch_bwd<64>(const BwdArgs&, bool, int, int, int, hipStream_t);
+template <> hipError_t launch_bwd<128>(const BwdArgs&, bool, int, int, int, hipStream_t);
 }  // namespace xattn
 
 namespace {
@@ -298,6 +301,57 @@ int run_split(Plan& p, int head_dim, int dtype, int num_splits, void* workspace,
   return launch_split(head_dim, p.a, m, dtype, p.mode, p.n_work, stream);
 }
 
+// ---- backward ---------------------------------------------------------------------------
+
+bool bwd_head_dim(int d) { return d == 64 || d == 128; }
+
+// Q-tile (= key-tile) slots per head of the backward kernels for a packed batch: an upper
+// bound on sum_s ceil(len_s / 128) that needs no lengths.
+long bwd_varlen_slots(int num_seqs, int max_seqlen, int total_tokens) {
+  constexpr int B = xattn::BwdShape::BR;
+  const long by_total = ((long)total_tokens + B - 1) / B + num_seqs;
+  const long by_max = (long)num_seqs * ((max_seqlen + B - 1) / B);
+  return by_total < by_max ? by_total : by_max;
+}
+
+size_t bwd_workspace_bytes(long rows) { return rows > 0 ? align256((size_t)rows * 4) : 0; }
+
+// The gradient-side arguments of a backward call (the forward-side ones went through a Plan).
+int check_bwd_pointers(const float* lse, const void* dout, void* dq, void* dk, void* dv) {
+  if (!lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
+}
+
+// Launch both backward kernels for a validated plan: `slots` q-tiles (= key tiles) per head,
+// over heads_q query heads and heads_q / kv_group key/value heads.
+int run_bwd(const Plan& p, int head_dim, int dtype, long slots, long heads_q, long outer,
+            const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace,
+            size_t workspace_size, void* stream) {
+  if (!workspace || !aligned(workspace, 256) || workspace_size < bwd_workspace_bytes(p.rows))
+    return ATTN_ERR_INVALID_ARG;
+  const long n_q = outer * heads_q * slots;
+  const long n_k = outer * (heads_q / p.a.kv_group) * slots;
+  if (slots > std::numeric_limits<int>::max() || n_q > std::numeric_limits<int>::max())
+    return ATTN_ERR_TOO_LARGE;
+  xattn::BwdArgs b{};
+  b.f = p.a;
+  b.f.tiles_per_head = (int)slots;
+  b.ktiles_per_head = (int)slots;
+  b.dout = static_cast<const uint16_t*>(dout);
+  b.dq = static_cast<uint16_t*>(dq);
+  b.dk = static_cast<uint16_t*>(dk);
+  b.dv = static_cast<uint16_t*>(dv);
+  b.dpsum = static_cast<float*>(workspace);
+  b.scale = scale;
+  const bool bf16 = dtype == ATTN_DTYPE_BF16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (head_dim == 64)
+    return hip_status(xattn::launch_bwd<64>(b, bf16, p.mode, (int)n_q, (int)n_k, s));
+  return hip_status(xattn::launch_bwd<128>(b, bf16, p.mode, (int)n_q, (int)n_k, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,12 +472,58 @@ int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o
   return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 
+size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen) {
+  if (batch <= 0 || heads_q <= 0 || seqlen <= 0) return 0;
+  return bwd_workspace_bytes((long)batch * heads_q * seqlen);
+}
+
+size_t attn_bwd_varlen_workspace_size(int total_tokens, int heads_q) {
+  if (total_tokens <= 0 || heads_q <= 0) return 0;
+  return bwd_workspace_bytes((long)heads_q * total_tokens);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int batch, int heads_q,
+             int heads_kv, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
+             int window_left, int window_right, void* workspace, size_t workspace_size,
+             void* stream) {
+  if (!bwd_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_dense(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), batch, heads_q,
+                      heads_kv, seqlen, head_dim, dtype, softmax_scale, causal, window_left,
+                      window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const int st = check_bwd_pointers(lse, dout, dq, dk, dv);
+  if (st != ATTN_OK) return st;
+  const long slots = ((long)seqlen + xattn::BwdShape::BR - 1) / xattn::BwdShape::BR;
+  return run_bwd(p, head_dim, dtype, slots, heads_q, batch, dout, dq, dk, dv, softmax_scale,
+                 workspace, workspace_size, stream);
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int heads_q, int heads_kv, int head_dim, int dtype, float softmax_scale,
+                    int causal, int window_left, int window_right, void* workspace,
+                    size_t workspace_size, void* stream) {
+  if (!bwd_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_varlen(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), cu_seqlens,
+                       num_seqs, max_seqlen, total_tokens, heads_q, heads_kv, head_dim, dtype,
+                       softmax_scale, causal, window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const int st = check_bwd_pointers(lse, dout, dq, dk, dv);
+  if (st != ATTN_OK) return st;
+  return run_bwd(p, head_dim, dtype, bwd_varlen_slots(num_seqs, max_seqlen, total_tokens),
+                 heads_q, 1, dout, dq, dk, dv, softmax_scale, workspace, workspace_size,
+                 stream);
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK: success";
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
     case ATTN_ERR_UNSUPPORTED_HEAD_DIM:
-      return "ATTN_ERR_UNSUPPORTED_HEAD_DIM: head_dim must be 64, 128, 256 or 512";
+      return "ATTN_ERR_UNSUPPORTED_HEAD_DIM: head_dim must be 64, 128, 256 or 512 (backward: "
+             "64 or 128)";
     case ATTN_ERR_UNSUPPORTED_DTYPE:
       return "ATTN_ERR_UNSUPPORTED_DTYPE: dtype must be ATTN_DTYPE_FP16 or ATTN_DTYPE_BF16";
     case ATTN_ERR_MISALIGNED:

@@ -1,0 +1,478 @@
+// gfx950 exact-attention backward: dQ, dK and dV from Q, K, V, O, the forward's LSE and dO.
+//
+// What is computed (page "mainloop_bwd_sm90_tma_gmma_ws.hpp", the backward `mma`): with
+// S = scale * Q K^T under the forward's mask and P recomputed from S and the stored LSE,
+//   P_ij = exp(S_ij - LSE_i),  dP = dO V^T,  dS = P * (dP - dPsum_i),
+//   dV = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K,
+// where dPsum_i = sum_j P_ij dP_ij = dO_i . O_i (the pages take it as an input; this library
+// forms it from dO and O).  With grouped K/V heads the dK and dV of a key/value head sum the
+// contributions of every query head of its group.
+//
+// Two kernels, both deterministic (no atomics):
+//  * attn_bwd_dq_kernel: one workgroup per q-tile, as the forward.  Each wave keeps its 32
+//    query rows of Q and dO in registers and sweeps the visible K/V tiles:
+//    S^T = K Q^T and dP^T = V dO^T (lane = query, as in the forward), dS^T from them, and
+//    dQ^T += K^T dS^T (the forward's O^T += V^T P^T with K in V's place).  It also writes
+//    dPsum for its rows, which the second kernel reads.
+//  * attn_bwd_dkdv_kernel: one workgroup per tile of 128 keys of one key/value head.  Each
+//    wave keeps its 32 key rows of K and V in registers and sweeps the visible q-tiles of every
+//    query head of the group: S = Q K^T and dP = dO V^T (lane = key), then
+//    dV^T += dO^T P and dK^T += Q^T dS.  The same building blocks as the forward, with the
+//    roles of queries and keys exchanged: the mask is the forward's with the window bounds
+//    swapped (key j sees query i iff j - window_right <= i <= j + window_left).
+// Tiles are staged global -> registers -> LDS, double-buffered.  An operand read both row-wise
+// (MFMA A operand) and transposed (ds_read_b64_tr_b16) is stored twice, once per swizzle.
+#pragma once
+
+#include "attn_common.h"
+
+namespace xattn {
+
+struct BwdArgs {
+  FwdArgs f;               // q, k, v, o (read), lse (read, natural log), sizes, mask, heads
+  const uint16_t* dout;    // dO, laid out as q
+  uint16_t* dq;            // laid out as q
+  uint16_t* dk;            // laid out as k
+  uint16_t* dv;            // laid out as v
+  float* dpsum;            // [rows of q]: written by the dQ kernel, read by the dK/dV kernel
+  float scale;             // softmax scale (dQ and dK are multiplied by it)
+  int ktiles_per_head;     // key-tile slots per key/value head (dK/dV kernel)
+};
+
+struct BwdShape {
+  static constexpr int NW = 4, NT = 256;
+  static constexpr int BR = 128;   // dQ kernel: query rows per workgroup
+  static constexpr int BC = 64;    // dQ kernel: keys per K/V tile
+  static constexpr int BK = 128;   // dK/dV kernel: keys per workgroup
+  static constexpr int BQ = 64;    // dK/dV kernel: query rows per Q/dO tile
+};
+
+// Sum of the eight products of two packed 16-bit vectors, in fp32.
+template <bool BF16>
+__device__ __forceinline__ float dot8(i32x4 x, i32x4 y) {
+  float acc = 0.f;
+  if constexpr (BF16) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, x), b = __builtin_bit_cast(bf16x8, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
+  } else {
+    const f16x8 a = __builtin_bit_cast(f16x8, x), b = __builtin_bit_cast(f16x8, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)a[i], (float)b[i], acc);
+  }
+  return acc;
+}
+
+// Stores the lane's row of a transposed accumulator (register r of column block db holds
+// d = 32 db + 8 (r / 4) + 4 hh + r % 4), multiplied by `mul` and rounded to 16 bits.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul,
+                                          int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& x = acc[db];
+      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * mul, x[4 * g4 + 1] * mul),
+                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * mul, x[4 * g4 + 3] * mul)};
+      *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
+    }
+}
+
+// Packs score-layout fp32 values (two 32-row blocks of 16 registers per 64) to the 16-bit
+// B operand of a transposed-accumulator product, as the forward packs P.
+template <bool BF16, int BN>
+__device__ __forceinline__ void pack_operand(const f32x16 (&s)[BN / 32], i32x4 (&pf)[BN / 16]) {
+#pragma unroll
+  for (int kc = 0; kc < BN / 16; ++kc) {
+    const int kb = kc >> 1, o8 = (kc & 1) * 8;
+    pf[kc] = (i32x4){(int)Elt<BF16>::pack2(s[kb][o8 + 0], s[kb][o8 + 1]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 4], s[kb][o8 + 5]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
+  }
+}
+
+constexpr float kBwdLog2e = 1.44269504088896340736f;
+
+// The forward's natural-log LSE in base-2 units; +inf for a row with no visible key (and for
+// rows past the end), so that exp2(s * c2 - lse2) is 0 there.
+__device__ __forceinline__ float lse_to_log2(float lse) {
+  return lse > -INFINITY ? lse * kBwdLog2e : INFINITY;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and dPsum)
+// ---------------------------------------------------------------------------------------------
+
+template <bool BF16, int D, int MODE>
+__global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_bwd_dq_kernel(BwdArgs ba) {
+  const FwdArgs& a = ba.f;
+  constexpr int BR = BwdShape::BR, BC = BwdShape::BC, NT = BwdShape::NT;
+  constexpr int CH = D / 8, ROWB = D * 2, TILEB = BC * ROWB, LPT = BC * CH / NT;
+  constexpr int STAGEB = 3 * TILEB;  // K (row-read swizzle), K (transpose swizzle), V
+  static_assert(BC * CH % NT == 0, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  Work w;
+  if (!decode_work<BR, MODE>(a, w)) return;
+  const int seqlen = w.seqlen;
+  int wl, wr;
+  mode_windows<MODE>(a, wl, wr);
+
+  const int q0 = w.tile * BR;
+  const int qw0 = q0 + wave * 32;
+  const int q_last = min(q0 + BR, seqlen) - 1;
+  int k_lo = 0, k_hi = seqlen - 1;
+  if (wl >= 0) k_lo = max(0, q0 - wl);
+  if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
+  const int t_lo = k_lo / BC, t_hi = k_hi / BC;
+
+  const bool wave_active = qw0 < seqlen;
+  const int qw_last = min(qw0 + 32, seqlen) - 1;
+  int kw_lo = 0, kw_hi = seqlen - 1;
+  if (wl >= 0) kw_lo = max(0, qw0 - wl);
+  if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
+
+  const uint16_t* __restrict__ kp = a.k + w.kv_row0 * D;
+  const uint16_t* __restrict__ vp = a.v + w.kv_row0 * D;
+  const int qrow = qw0 + l32;
+  const long grow = w.row0 + qrow;  // global row of the lane's query
+
+  i32x4 qf[D / 16], dof[D / 16];
+  load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
+  load_q<D>(ba.dout + w.row0 * D, qrow, seqlen, hh, dof);
+  float dps;
+  {
+    i32x4 of[D / 16];
+    load_q<D>(a.o + w.row0 * D, qrow, seqlen, hh, of);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) part += dot8<BF16>(dof[c], of[c]);
+    dps = halves_sum(part);
+  }
+  if (hh == 0 && qrow < seqlen) ba.dpsum[grow] = dps;
+  const float lse2 = qrow < seqlen ? lse_to_log2(a.lse[grow]) : INFINITY;
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const float c2 = a.scale_log2;
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
+
+  i32x4 stage_k[LPT], stage_v[LPT];
+  auto gload = [&](int t) {
+    const int kbase = t * BC;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      const int key = kbase + r;
+      if (key < seqlen) {
+        stage_k[u] = ((const i32x4*)(kp + (long)key * D))[c];
+        stage_v[u] = ((const i32x4*)(vp + (long)key * D))[c];
+      } else {  // past the end: zeros (those keys are masked)
+        stage_k[u] = (i32x4){0, 0, 0, 0};
+        stage_v[u] = (i32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int s) {
+    char* kn = smem + s * STAGEB;
+    char* kt = kn + TILEB;
+    char* vn = kt + TILEB;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      *(i32x4*)(kn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_k[u];
+      *(i32x4*)(kt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_k[u];
+      *(i32x4*)(vn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_v[u];
+    }
+  };
+
+  auto consume = [&](int t, int s) {
+    const int k0 = t * BC;
+    if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;
+    const char* kn = smem + s * STAGEB;
+    const char* kt = kn + TILEB;
+    const char* vn = kt + TILEB;
+    f32x16 sacc[BC / 32], dpacc[BC / 32];
+    mma_scores<BF16, D, BC>(kn, lo, qf, sacc);
+    const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
+                           (wl >= 0 && k0 < qw0 + 31 - wl);
+    if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+    mma_scores<BF16, D, BC>(vn, lo, dof, dpacc);
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
+        sacc[kb][r] = p * (dpacc[kb][r] - dps);  // dS^T
+      }
+    i32x4 dsf[BC / 16];
+    pack_operand<BF16, BC>(sacc, dsf);
+    mma_pv<BF16, D, BC>(kt, lo, dsf, dqacc);
+  };
+
+  gload(t_lo);
+  lstore(0);
+  __syncthreads();
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int s = (t - t_lo) & 1;
+    if (t < t_hi) gload(t + 1);
+    consume(t, s);
+    if (t < t_hi) lstore(s ^ 1);
+    __syncthreads();
+  }
+
+  if (wave_active && qrow < seqlen) store_row<BF16, D>(ba.dq + grow * D, dqacc, ba.scale, hh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK and dV
+// ---------------------------------------------------------------------------------------------
+
+struct KeyWork {
+  int tile;       // key-tile index within the sequence
+  int seqlen;
+  long kv_row0;   // row of the sequence's token 0 in the k/v row space
+  long q_row0;    // the same in the q row space, for the group's first query head
+  long q_stride;  // rows between consecutive query heads
+};
+
+// Map this workgroup to (key tile, key/value head, batch | sequence).  Key tiles run in
+// ascending order: under a causal mask the first ones are seen by the most queries.
+template <int BK>
+__device__ __forceinline__ bool decode_key_work(const BwdArgs& ba, KeyWork& w) {
+  const FwdArgs& a = ba.f;
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = ba.ktiles_per_head;
+  const int g = a.kv_group;
+  if (a.cu_seqlens == nullptr) {
+    const int bh = wid / per;  // (batch, key/value head)
+    w.tile = wid - bh * per;
+    w.seqlen = a.seqlen;
+    w.kv_row0 = (long)bh * a.seqlen;
+    w.q_row0 = (long)bh * g * a.seqlen;  // query head (b, kvh * g) = row block b*Hq + kvh*g
+    w.q_stride = a.seqlen;
+    return true;
+  }
+  const int h = wid / per;
+  const int slot = wid - h * per;
+  int acc = 0;
+  int c_prev = min(max(a.cu_seqlens[0], 0), a.total_tokens);
+  for (int s = 0; s < a.num_seqs; ++s) {
+    const int c_next = min(max(a.cu_seqlens[s + 1], c_prev), a.total_tokens);
+    const int nt = (c_next - c_prev + BK - 1) / BK;
+    if (slot < acc + nt) {
+      w.tile = slot - acc;
+      w.seqlen = c_next - c_prev;
+      w.kv_row0 = (long)h * a.total_tokens + c_prev;
+      w.q_row0 = (long)h * g * a.total_tokens + c_prev;
+      w.q_stride = a.total_tokens;
+      return true;
+    }
+    acc += nt;
+    c_prev = c_next;
+  }
+  return false;
+}
+
+template <bool BF16, int D, int MODE>
+__global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_bwd_dkdv_kernel(BwdArgs ba) {
+  const FwdArgs& a = ba.f;
+  constexpr int BK = BwdShape::BK, BQ = BwdShape::BQ, NT = BwdShape::NT;
+  constexpr int CH = D / 8, ROWB = D * 2, TILEB = BQ * ROWB, LPT = BQ * CH / NT;
+  // per stage: Q (row-read swizzle), Q (transpose swizzle), dO (both), LSE2 and dPsum rows
+  constexpr int STAGEB = 4 * TILEB + 2 * BQ * 4;
+  static_assert(BQ * CH % NT == 0 && BQ <= NT, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  KeyWork w;
+  if (!decode_key_work<BK>(ba, w)) return;
+  const int seqlen = w.seqlen;
+  int wl, wr;
+  mode_windows<MODE>(a, wl, wr);
+
+  const int k0 = w.tile * BK;
+  const int kw0 = k0 + wave * 32;
+  const int k_last = min(k0 + BK, seqlen) - 1;
+  int q_lo = 0, q_hi = seqlen - 1;  // queries that see any key of the workgroup
+  if (wr >= 0) q_lo = max(0, k0 - wr);
+  if (wl >= 0) q_hi = min(seqlen - 1, k_last + wl);
+  const int qt_lo = q_lo / BQ, nq = q_hi / BQ - qt_lo + 1;
+  const int n_it = a.kv_group * nq;  // (query head of the group, q-tile) pairs
+
+  const bool wave_active = kw0 < seqlen;
+  const int kw_last = min(kw0 + 32, seqlen) - 1;
+  int qw_lo = 0, qw_hi = seqlen - 1;  // queries that see any key of this wave
+  if (wr >= 0) qw_lo = max(0, kw0 - wr);
+  if (wl >= 0) qw_hi = min(seqlen - 1, kw_last + wl);
+
+  const int krow = kw0 + l32;
+  i32x4 kf[D / 16], vf[D / 16];
+  load_q<D>(a.k + w.kv_row0 * D, krow, seqlen, hh, kf);
+  load_q<D>(a.v + w.kv_row0 * D, krow, seqlen, hh, vf);
+  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const float c2 = a.scale_log2;
+
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dkacc[db][r] = 0.f;
+      dvacc[db][r] = 0.f;
+    }
+
+  i32x4 stage_q[LPT], stage_d[LPT];
+  float stage_l = INFINITY, stage_p = 0.f;
+  auto gload = [&](int it) {
+    const int j = it / nq;
+    const int qbase = (qt_lo + it - j * nq) * BQ;
+    const long hrow = w.q_row0 + j * w.q_stride;  // row of token 0 of query head j
+    const uint16_t* qp = a.q + hrow * D;
+    const uint16_t* dp = ba.dout + hrow * D;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      const int q = qbase + r;
+      if (q < seqlen) {
+        stage_q[u] = ((const i32x4*)(qp + (long)q * D))[c];
+        stage_d[u] = ((const i32x4*)(dp + (long)q * D))[c];
+      } else {
+        stage_q[u] = (i32x4){0, 0, 0, 0};
+        stage_d[u] = (i32x4){0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int q = qbase + tid;
+      stage_l = q < seqlen ? lse_to_log2(a.lse[hrow + q]) : INFINITY;
+      stage_p = q < seqlen ? ba.dpsum[hrow + q] : 0.f;
+    }
+  };
+  auto lstore = [&](int s) {
+    char* qn = smem + s * STAGEB;
+    char* qt = qn + TILEB;
+    char* dn = qt + TILEB;
+    char* dt = dn + TILEB;
+    float* ls = (float*)(dt + TILEB);
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      *(i32x4*)(qn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_q[u];
+      *(i32x4*)(qt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_q[u];
+      *(i32x4*)(dn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_d[u];
+      *(i32x4*)(dt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_d[u];
+    }
+    if (tid < BQ) {
+      ls[tid] = stage_l;
+      ls[BQ + tid] = stage_p;
+    }
+  };
+
+  auto consume = [&](int it, int s) {
+    const int j = it / nq;
+    const int qbase = (qt_lo + it - j * nq) * BQ;
+    if (!wave_active || qbase > qw_hi || qbase + BQ - 1 < qw_lo) return;
+    const char* qn = smem + s * STAGEB;
+    const char* qt = qn + TILEB;
+    const char* dn = qt + TILEB;
+    const char* dt = dn + TILEB;
+    const float* ls = (const float*)(dt + TILEB);
+    f32x16 sacc[BQ / 32], dpacc[BQ / 32];
+    mma_scores<BF16, D, BQ>(qn, lo, kf, sacc);  // S[query, key]: lane = key
+    const bool need_mask = (qbase + BQ > seqlen) || (wr >= 0 && qbase < kw0 + 31 - wr) ||
+                           (wl >= 0 && qbase + BQ - 1 > kw0 + wl);
+    // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the
+    // window bounds exchanged
+    if (need_mask) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
+    mma_scores<BF16, D, BQ>(dn, lo, vf, dpacc);  // dP[query, key]
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // register 4 g4 + i of block qb holds query 32 qb + 8 g4 + 4 hh + i
+        const f32x4 l2 = *(const f32x4*)(ls + 32 * qb + 8 * g4 + 4 * hh);
+        const f32x4 dd = *(const f32x4*)(ls + BQ + 32 * qb + 8 * g4 + 4 * hh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;
+          const float p = fast_exp2(fmaf(sacc[qb][r], c2, -l2[i]));
+          sacc[qb][r] = p;
+          dpacc[qb][r] = p * (dpacc[qb][r] - dd[i]);  // dS
+        }
+      }
+    i32x4 pf[BQ / 16], dsf[BQ / 16];
+    pack_operand<BF16, BQ>(sacc, pf);
+    pack_operand<BF16, BQ>(dpacc, dsf);
+    mma_pv<BF16, D, BQ>(dt, lo, pf, dvacc);   // dV^T += dO^T P
+    mma_pv<BF16, D, BQ>(qt, lo, dsf, dkacc);  // dK^T += Q^T dS
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < n_it; ++it) {
+    const int s = it & 1;
+    if (it + 1 < n_it) gload(it + 1);
+    consume(it, s);
+    if (it + 1 < n_it) lstore(s ^ 1);
+    __syncthreads();
+  }
+
+  if (wave_active && krow < seqlen) {
+    store_row<BF16, D>(ba.dk + (w.kv_row0 + krow) * D, dkacc, ba.scale, hh);
+    store_row<BF16, D>(ba.dv + (w.kv_row0 + krow) * D, dvacc, 1.0f, hh);
+  }
+}
+
+// Host launchers for one head dim (explicitly specialised per head dim in its own translation
+// unit): the dQ kernel over n_q workgroups, then the dK/dV kernel over n_k, on one stream.
+template <int D>
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int mode, int n_q, int n_k,
+                      hipStream_t stream);
+
+template <bool BF16, int D, int MODE>
+hipError_t launch_bwd_mode(const BwdArgs& a, int n_q, int n_k, hipStream_t s) {
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, MODE>), dim3(n_q), dim3(BwdShape::NT), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, MODE>), dim3(n_k), dim3(BwdShape::NT), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+#define XATTN_DEFINE_BWD_LAUNCHER(D)                                                         \
+  template <>                                                                                \
+  hipError_t launch_bwd<D>(const BwdArgs& a, bool bf16, int mode, int n_q, int n_k,          \
+                           hipStream_t s) {                                                  \
+    if (bf16) {                                                                              \
+      if (mode == MASK_NONE) return launch_bwd_mode<true, D, MASK_NONE>(a, n_q, n_k, s);     \
+      if (mode == MASK_CAUSAL) return launch_bwd_mode<true, D, MASK_CAUSAL>(a, n_q, n_k, s); \
+      return launch_bwd_mode<true, D, MASK_WINDOW>(a, n_q, n_k, s);                          \
+    }                                                                                        \
+    if (mode == MASK_NONE) return launch_bwd_mode<false, D, MASK_NONE>(a, n_q, n_k, s);      \
+    if (mode == MASK_CAUSAL) return launch_bwd_mode<false, D, MASK_CAUSAL>(a, n_q, n_k, s);  \
+    return launch_bwd_mode<false, D, MASK_WINDOW>(a, n_q, n_k, s);                           \
+  }
+
+}  // namespace xattn

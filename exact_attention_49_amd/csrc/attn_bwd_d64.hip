@@ -1,0 +1,6 @@
+// Backward kernel instantiations for head_dim = 64 (all dtypes and mask modes).
+#include "attn_bwd.h"
+
+namespace xattn {
+XATTN_DEFINE_BWD_LAUNCHER(64)
+}  // namespace xattn

@@ -18,7 +18,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_dense", "make_varlen", "make_workload"]
+__all__ = ["Workload", "WORKLOADS", "make_dense", "make_varlen", "make_workload",
+           "make_upstream"]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
@@ -47,6 +48,7 @@ class Workload:
     value_scale: float = 1.0
     heads_kv: int = 0       # key/value heads (grouped-query attention); 0: as many as `heads`
     splitkv: bool = False   # run through the split-KV entry point
+    backward: bool = False  # time the backward pass (dO drawn with seed + 100)
     note: str = field(default="", compare=False)
 
     @property
@@ -95,6 +97,10 @@ WORKLOADS = {
                  seqlen=8192, head_dim=128, dtype="bf16", causal=True, seed=4907,
                  value_scale=0.5,
                  note="B=2 Hq=32 Hkv=8 N=8192 d=128 bf16 causal, inputs N(0,1)*0.5"),
+        # the backward pass on the forward benchmark's shape
+        Workload("bwd_causal_bf16_d128_n8192", batch=2, heads=32, seqlen=8192, head_dim=128,
+                 dtype="bf16", causal=True, seed=4903, value_scale=0.5, backward=True,
+                 note="backward of B=2 H=32 N=8192 d=128 bf16 causal (dQ, dK, dV)"),
     ]
 }
 
@@ -145,3 +151,13 @@ def make_workload(w: Workload):
                            w.seed, w.value_scale, heads_kv=w.heads_kv)
     return make_dense(w.batch, w.heads, w.seqlen, w.head_dim, w.dtype, w.seed, w.value_scale,
                       heads_kv=w.heads_kv)
+
+
+def make_upstream(shape, dtype: str, seed: int, value_scale: float = 1.0):
+    """An upstream gradient dO of the given shape: `randn` in float32 from a CPU generator
+    seeded with `seed`, times the value scale, cast to the I/O dtype (as Q, K, V)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=gen, dtype=torch.float32)
+    if value_scale != 1.0:
+        x = x * value_scale
+    return x.to(_DTYPES[dtype])

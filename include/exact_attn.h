@@ -1,5 +1,6 @@
 /*
- * exact_attn.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ * exact_attn.h - C ABI of the MI355X (gfx950) exact-attention library (forward, and the
+ * backward at the end of this file).
  *
  * The library computes the FlashAttention-2 forward pass (page "flash_attn_mma_tiling_qk.cu",
  * header comment and kernel: each block takes a tile of Q rows, streams every K/V tile of the
@@ -51,7 +52,7 @@ enum {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,          /* null pointer, bad size, scale or mask argument      */
-  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 2, /* head_dim not in {64, 128, 256, 512}                 */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 2, /* head_dim not in {64, 128, 256, 512} (bwd: 64, 128)  */
   ATTN_ERR_UNSUPPORTED_DTYPE = 3,    /* dtype not fp16 / bf16                               */
   ATTN_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte or lse/cu_seqlens not 4-byte    */
   ATTN_ERR_TOO_LARGE = 5,            /* a size would overflow the kernel's index arithmetic */
@@ -162,6 +163,45 @@ size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int 
 int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim);
 int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
                                        int heads, int head_dim);
+
+/*
+ * Backward pass: the gradients dQ, dK, dV of a loss L given dO = dL/dO, for the forward that
+ * the same arguments describe (page "mainloop_bwd_sm90_tma_gmma_ws.hpp", the backward `mma`:
+ * P is recomputed from the scores and the stored LSE, dP = dO V^T,
+ * dS = P * (dP - dPsum) with dPsum_i = dO_i . O_i, dV = P^T dO, dK = scale * dS^T Q and
+ * dQ = scale * dS K).  With grouped heads the dK, dV of a key/value head are summed over the
+ * query heads of its group.
+ *   q, k, v, heads, mask, scale : as for attn_fwd_gqa / attn_fwd_varlen_gqa (heads_kv =
+ *                   heads_q for plain multi-head attention).
+ *   o, lse        : the forward's output and its natural-log LSE for these inputs (lse is
+ *                   required here; layouts as in the forward).
+ *   dout          : dO, laid out as o.  dq is laid out as q; dk and dv as k and v.  All
+ *                   16-byte aligned DEVICE arrays owned by the caller; dq, dk, dv are fully
+ *                   overwritten and must not alias any input.
+ *   workspace     : DEVICE memory owned by the caller, 256-byte aligned, of at least
+ *                   attn_bwd_workspace_size / attn_bwd_varlen_workspace_size bytes (one fp32
+ *                   per query row: dPsum); otherwise ATTN_ERR_INVALID_ARG.  Its contents on
+ *                   entry do not matter; two calls in flight at once must not share it.
+ *   head_dim      : 64 or 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ * Two kernels run on `stream`, deterministically (no atomics).  Other errors as for the
+ * forward.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int batch, int heads_q,
+             int heads_kv, int seqlen, int head_dim, int dtype, float softmax_scale, int causal,
+             int window_left, int window_right, void* workspace, size_t workspace_size,
+             void* stream);
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int heads_q, int heads_kv, int head_dim, int dtype, float softmax_scale,
+                    int causal, int window_left, int window_right, void* workspace,
+                    size_t workspace_size, void* stream);
+
+/* Workspace bytes of a backward call (0 for an empty problem).  Host-only. */
+size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen);
+size_t attn_bwd_varlen_workspace_size(int total_tokens, int heads_q);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -244,3 +244,53 @@ def test_binding_gqa_checks_shapes():
     q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(binding.AttnError, match="GPU tensor"):
         binding.attn_fwd_gqa(q, q[:, :2], q[:, :2])
+
+
+# ---- backward entry points (host-side validation and workspace sizing only) ------------------
+
+def call_bwd(lib, ws=A, wsb=1 << 30, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, b=1, hq=2, hkv=1, n=256,
+                d=128, dtype=1, scale=SCALE, causal=1, wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_bwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["do"],
+                        args["dq"], args["dk"], args["dv"], args["b"], args["hq"], args["hkv"],
+                        args["n"], args["d"], args["dtype"], args["scale"], args["causal"],
+                        args["wl"], args["wr"], ws, wsb, None)
+
+
+def call_bwd_varlen(lib, ws=A, wsb=1 << 30, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, cu=A, ns=2, maxs=8,
+                total=16, hq=2, hkv=2, d=64, dtype=0, scale=SCALE, causal=0, wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_bwd_varlen(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                               args["do"], args["dq"], args["dk"], args["dv"], args["cu"],
+                               args["ns"], args["maxs"], args["total"], args["hq"], args["hkv"],
+                               args["d"], args["dtype"], args["scale"], args["causal"],
+                               args["wl"], args["wr"], ws, wsb, None)
+
+
+@pytest.mark.parametrize("call", [call_bwd, call_bwd_varlen])
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(q=None), 1), (dict(o=None), 1),
+    (dict(d=256), 2), (dict(d=512), 2), (dict(d=96), 2), (dict(dtype=3), 3),
+    (dict(do=A + 4), 4), (dict(dq=A + 2), 4), (dict(dv=A + 8), 4), (dict(lse=A + 2), 4),
+    (dict(hq=4, hkv=3), 1), (dict(scale=0.0), 1), (dict(causal=2), 1),
+    (dict(ws=None), 1), (dict(ws=A + 16), 1), (dict(wsb=4), 1),
+])
+def test_bwd_rejects_bad_arguments(lib, call, kw, status):
+    assert call(lib, **kw) == status
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.attn_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 4
+    assert lib.attn_bwd_workspace_size(1, 3, 5) == 256          # 60 bytes, 256-byte granules
+    assert lib.attn_bwd_workspace_size(0, 3, 5) == 0
+    assert lib.attn_bwd_varlen_workspace_size(1000, 6) == 24064
+    assert lib.attn_bwd_varlen_workspace_size(0, 6) == 0
+
+
+def test_bwd_empty_problem_is_a_no_op(lib):
+    assert call_bwd(lib, b=0, ws=None, wsb=0) == 0
+    assert call_bwd_varlen(lib, ns=0, ws=None, wsb=0) == 0
+    assert call_bwd(lib, b=0, d=256) == 2   # non-size arguments are still checked

@@ -1,0 +1,172 @@
+"""GPU parity of the backward entry points (through the C ABI) against the fp64 CPU oracle.
+
+The GPU path runs as a user would run it: the library's forward produces O and the LSE, then
+the backward takes them with dO.  The oracle computes the exact gradients from Q, K, V and dO
+alone.  Bar, per gradient tensor G: max |G_gpu - G_ref| <= TOL[dtype] * max |G_ref|, with the
+forward's bounds (2e-2 bf16, 5e-3 fp16) taken relative to the gradient's largest magnitude
+(gradients have no natural unit scale as O does; the reasoning is in the design notes).
+
+Cases: both head dims and dtypes, every mask mode at a ragged length, GQA and MQA, packed
+batches with empty and one-token sequences, multi-tile grids, determinism, and one head of the
+benchmark shape at full length."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_49_amd import (attn_bwd, attn_bwd_varlen, attn_fwd_gqa,
+                                    attn_fwd_varlen_gqa, inputs)
+from tests.gpu_helpers import to64
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+TOL = {torch.bfloat16: 2e-2, torch.float16: 5e-3}
+MASKS = {
+    "none": dict(causal=False, wl=-1, wr=-1),
+    "causal": dict(causal=True, wl=-1, wr=-1),
+    "window_40_0": dict(causal=True, wl=40, wr=0),
+    "window_30_70": dict(causal=False, wl=30, wr=70),
+}
+DEV = torch.device("cuda:0")
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _check(got, ref, dtype, what):
+    worst = 0.0
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = to64(g)
+        assert g.shape == r.shape, f"{what} {name} shape"
+        assert np.all(np.isfinite(g)), f"{what} {name}: non-finite"
+        scale = float(np.max(np.abs(r))) if r.size else 0.0
+        err = float(np.max(np.abs(g - r))) if r.size else 0.0
+        assert err <= TOL[dtype] * scale + 1e-6, \
+            f"{what} {name}: max err {err:.3e} > {TOL[dtype]} * {scale:.3e}"
+        worst = max(worst, err / scale if scale else 0.0)
+    return worst
+
+
+def _gpu_dense(q, k, v, do, m):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = attn_fwd_gqa(qd, kd, vd, causal=m["causal"], window_left=m["wl"],
+                          window_right=m["wr"])
+    g = attn_bwd(qd, kd, vd, o, lse, dod, causal=m["causal"], window_left=m["wl"],
+                 window_right=m["wr"])
+    torch.cuda.synchronize()
+    return g
+
+
+def _ref_dense(q, k, v, do, d, m):
+    return oracle.attention_backward_dense(q.double().numpy(), k.double().numpy(),
+                                           v.double().numpy(), do.double().numpy(),
+                                           1 / math.sqrt(d), m["causal"], m["wl"], m["wr"])
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("dtype", list(DTYPES))
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_dense_all_modes(d, dtype, mask):
+    _announce(f"bwd dense d={d} {dtype} {mask}")
+    m = MASKS[mask]
+    q, k, v = inputs.make_dense(2, 2, 300, d, dtype, seed=2000 + d)
+    do = inputs.make_upstream(q.shape, dtype, seed=2100 + d)
+    got = _gpu_dense(q, k, v, do, m)
+    _check(got, _ref_dense(q, k, v, do, d, m), DTYPES[dtype], f"d={d} {dtype} {mask}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 33, 64, 127, 128, 129, 257])
+def test_bwd_ragged_lengths(n):
+    _announce(f"bwd ragged n={n}")
+    m = MASKS["causal"]
+    q, k, v = inputs.make_dense(1, 2, n, 128, "bf16", seed=2200 + n)
+    do = inputs.make_upstream(q.shape, "bf16", seed=2300 + n)
+    _check(_gpu_dense(q, k, v, do, m), _ref_dense(q, k, v, do, 128, m), torch.bfloat16,
+           f"n={n}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 1), (8, 8)])
+@pytest.mark.parametrize("mask", ["causal", "window_30_70"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_gqa(d, mask, hq, hkv):
+    _announce(f"bwd gqa d={d} {mask} {hq}/{hkv}")
+    m = MASKS[mask]
+    q, k, v = inputs.make_dense(1, hq, 200, d, "fp16", seed=2400 + hq + d, heads_kv=hkv)
+    do = inputs.make_upstream(q.shape, "fp16", seed=2500 + hq)
+    _check(_gpu_dense(q, k, v, do, m), _ref_dense(q, k, v, do, d, m), torch.float16,
+           f"gqa {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal", "window_40_0"])
+def test_bwd_varlen(d, mask):
+    _announce(f"bwd varlen d={d} {mask}")
+    m = MASKS[mask]
+    lens = [1, 0, 64, 300, 129, 3, 200]
+    q, k, v, cu = inputs.make_varlen(len(lens), 0, 0, 6, d, "bf16", seed=2600 + d, lengths=lens,
+                                     heads_kv=2)
+    do = inputs.make_upstream(q.shape, "bf16", seed=2700 + d)
+    qd, kd, vd, dod, cud = (x.to(DEV) for x in (q, k, v, do, cu))
+    o, lse = attn_fwd_varlen_gqa(qd, kd, vd, cud, max(lens), causal=m["causal"],
+                                 window_left=m["wl"], window_right=m["wr"])
+    got = attn_bwd_varlen(qd, kd, vd, o, lse, dod, cud, max(lens), causal=m["causal"],
+                          window_left=m["wl"], window_right=m["wr"])
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_varlen(q.double().numpy(), k.double().numpy(),
+                                           v.double().numpy(), do.double().numpy(), cu.numpy(),
+                                           1 / math.sqrt(d), m["causal"], m["wl"], m["wr"])
+    _check(got, ref, torch.bfloat16, f"varlen d={d} {mask}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_multi_tile_grid(d):
+    _announce(f"bwd multi-tile d={d}")
+    m = MASKS["causal"]
+    q, k, v = inputs.make_dense(2, 4, 1100, d, "bf16", seed=2800 + d, value_scale=0.5)
+    do = inputs.make_upstream(q.shape, "bf16", seed=2900 + d)
+    _check(_gpu_dense(q, k, v, do, m), _ref_dense(q, k, v, do, d, m), torch.bfloat16,
+           f"multi-tile d={d}")
+
+
+def test_bwd_is_deterministic():
+    _announce("bwd determinism")
+    m = MASKS["causal"]
+    q, k, v = inputs.make_dense(1, 8, 777, 128, "bf16", seed=3000, heads_kv=2)
+    do = inputs.make_upstream(q.shape, "bf16", seed=3001)
+    a = _gpu_dense(q, k, v, do, m)
+    b = _gpu_dense(q, k, v, do, m)
+    for x, y in zip(a, b):
+        assert torch.equal(x.cpu(), y.cpu())
+
+
+def test_bwd_full_length_head_of_benchmark_shape():
+    """B=2 H=32 N=8192 d=128 causal bf16 on the GPU; two (batch, head) pairs against the
+    oracle in full (with plain multi-head attention a head's gradients depend only on it)."""
+    w = inputs.WORKLOADS["causal_bf16_d128_n8192"]
+    _announce("bwd " + w.name)
+    q, k, v = inputs.make_workload(w)
+    do = inputs.make_upstream(q.shape, w.dtype, seed=w.seed + 100, value_scale=w.value_scale)
+    m = dict(causal=w.causal, wl=w.window_left, wr=w.window_right)
+    dq, dk, dv = (g.cpu() for g in _gpu_dense(q, k, v, do, m))
+    for (b, h) in [(0, 0), (1, 31)]:
+        ref = oracle.attention_head_backward(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                             v[b, h].double().numpy(),
+                                             do[b, h].double().numpy(), w.softmax_scale,
+                                             w.causal, w.window_left, w.window_right)
+        _check((dq[b, h], dk[b, h], dv[b, h]), ref, torch.bfloat16, f"{w.name} ({b},{h})")
+
+
+def test_bwd_binding_errors():
+    from exact_attention_49_amd import AttnError
+    q = torch.zeros(1, 2, 16, 256, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(1, 2, 16, dtype=torch.float32, device=DEV)
+    with pytest.raises(AttnError):
+        attn_bwd(q, q, q, q, lse, q)   # head_dim 256 has no backward
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(AttnError):
+        attn_bwd(q, q, q, q, lse, q[:, :1].contiguous())   # dO shape
