@@ -38,7 +38,8 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d, halved if causal) and % of MFMA peak"
 METRIC_BWD = ("attention bwd TFLOP/s (2.5·4·B·H·N²·d, halved if causal) and % of MFMA peak")
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6}    # MI355X dense MFMA, AMD's published figure
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6,    # MI355X dense MFMA, AMD's published figures
+               "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_bf16_d128_n8192"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -89,6 +90,8 @@ def workload_bytes(w, cu=None) -> float:
     LSE written once (4 B per row); K and V have the key/value head count.  Backward: Q, K, V,
     O, dO read, dQ, dK, dV written (2 B each), LSE read, dPsum written and read (4 B each)."""
     tokens = int(cu[-1]) if w.varlen else w.batch * w.seqlen
+    if w.fp8:  # 1-byte Q, K, V; 2-byte O
+        return tokens * (w.heads * (w.head_dim * 3 + 4) + w.kv_heads * 2 * w.head_dim)
     if w.backward:
         return tokens * (w.heads * (4 * w.head_dim * 2 + 12) + w.kv_heads * 4 * w.head_dim * 2)
     return tokens * (w.heads * (2 * w.head_dim * 2 + 4) + w.kv_heads * 2 * w.head_dim * 2)
@@ -100,6 +103,8 @@ def kernel_name(w, cu=None) -> str:
     once the grid of 256-row tiles has at least 1024 workgroups, else the generic one)."""
     if w.backward:
         return "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel (one step)"
+    if w.fp8:
+        return "attn_fwd_fp8_kernel"
     if w.splitkv:  # one step = the split sweep and the merge
         base = "attn_fwd_wide_kernel" if w.head_dim >= 256 else "attn_fwd_kernel"
         return f"{base} (split-KV) + attn_merge_kernel"
@@ -223,6 +228,11 @@ def inputs_upstream(w, q):
     return inputs.make_upstream(q.shape, w.dtype, seed=w.seed + 100, value_scale=w.value_scale)
 
 
+def inputs_dequantized(codes, descale):
+    """What E4M3 codes stand for (code * descale), as float32 CPU tensors for the oracle."""
+    return codes.float() * float(descale)
+
+
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
     import torch
     dev = torch.device("cuda:0")
@@ -266,7 +276,8 @@ def main() -> int:
 
     import torch
 
-    from exact_attention_49_amd import (attn_bwd, attn_fwd, attn_fwd_gqa, attn_fwd_splitkv,
+    from exact_attention_49_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_gqa,
+                                        attn_fwd_splitkv,
                                         attn_fwd_varlen, attn_fwd_varlen_gqa,
                                         splitkv_num_splits, splitkv_workspace_size)
     w = inputs.WORKLOADS[args.workload]
@@ -288,6 +299,12 @@ def main() -> int:
     if w.splitkv:  # caller-owned workspace, allocated before any timing
         nbytes = splitkv_workspace_size(w.batch, w.heads, w.seqlen, w.head_dim, 0)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if w.fp8:  # E4M3 inputs with per-tensor descales, quantised before timing
+        (q8, dsq), (k8, dsk), (v8, dsv) = (inputs.quantize_fp8(x) for x in (q, k, v))
+        qd, kd, vd = q8.to(dev), k8.to(dev), v8.to(dev)
+        descales = [torch.tensor([x], dtype=torch.float32, device=dev) for x in (dsq, dsk, dsv)]
+        od = torch.empty(q.shape, dtype=w.torch_dtype, device=dev)
+        q, k, v = (inputs_dequantized(x, s) for x, s in ((q8, dsq), (k8, dsk), (v8, dsv)))
     if w.backward:  # the forward's outputs, dO, gradient buffers and workspace, before timing
         attn_fwd_gqa(qd, kd, vd, causal=w.causal, window_left=w.window_left,
                      window_right=w.window_right, out=od, lse=lsed)
@@ -296,7 +313,11 @@ def main() -> int:
         ws = torch.empty(od.numel() // w.head_dim * 4 + 256, dtype=torch.uint8, device=dev)
 
     def step():
-        if w.backward:
+        if w.fp8:
+            attn_fwd_fp8(qd, kd, vd, *descales, causal=w.causal, window_left=w.window_left,
+                         window_right=w.window_right, out_dtype=w.torch_dtype, out=od,
+                         lse=lsed)
+        elif w.backward:
             attn_bwd(qd, kd, vd, od, lsed, dod, causal=w.causal, window_left=w.window_left,
                      window_right=w.window_right, dq=dqd, dk=dkd, dv=dvd, workspace=ws)
         elif w.splitkv:
@@ -356,7 +377,7 @@ def main() -> int:
     algo_bytes = workload_bytes(w, cu)
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    peak = PEAK_TFLOPS["fp8" if w.fp8 else w.dtype]
     traffic = load_traffic(w)
 
     config = {"workload": w.name, "heads": w.heads, "heads_kv": w.kv_heads,
@@ -380,7 +401,8 @@ def main() -> int:
     out = {
         "metric": METRIC_BWD if w.backward else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if w.fp8 else w.dtype,
         "data": "synthetic (seeded N(0,1) inputs, no dataset)", "config": config,
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "flops_per_step": flops, "cache": "flushed 512 MiB between steps" if args.flush

@@ -18,7 +18,7 @@ __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd
            "attn_fwd_splitkv",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "attn_bwd",
-           "attn_bwd_varlen", "library_path",
+           "attn_bwd_varlen", "attn_fwd_fp8", "attn_fwd_varlen_fp8", "library_path",
            "load_library", "STATUS", "EXPORTED_SYMBOLS"]
 
 LIB_NAME = "libexact_attn.so"
@@ -52,6 +52,8 @@ EXPORTED_SYMBOLS = {
     "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "attn_fwd_fp8": (_I, [_P] * 8 + [_I] * 6 + [_F] + [_I] * 3 + [_P]),
+    "attn_fwd_varlen_fp8": (_I, [_P] * 9 + [_I] * 7 + [_F] + [_I] * 3 + [_P]),
     "attn_bwd": (_I, [_P] * 9 + [_I] * 6 + [_F] + [_I] * 3 + [_P, _S, _P]),
     "attn_bwd_varlen": (_I, [_P] * 10 + [_I] * 7 + [_F] + [_I] * 3 + [_P, _S, _P]),
     "attn_bwd_workspace_size": (_S, [_I, _I, _I]),
@@ -404,3 +406,102 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
                              _stream_handle(q.device))
     _check(st, "attn_bwd_varlen")
     return dq, dk, dv
+
+
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)   # E4M3 codes (uint8: the raw bytes)
+
+
+def _fp8_inputs(q, k, v, dims):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+        if t.dtype not in FP8_DTYPES:
+            raise AttnError(f"{n} must hold E4M3 codes (torch.float8_e4m3fn or uint8)")
+    if q.dim() != dims or k.dim() != dims or v.shape != k.shape:
+        raise AttnError("q and k, v have the wrong number of dimensions or k, v differ")
+
+
+def _descales(descale_q, descale_k, descale_v):
+    out = []
+    for t, n in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):
+        if t is None:
+            out.append(None)
+            continue
+        _device_tensor(t, n)
+        if t.dtype != torch.float32 or t.numel() != 1:
+            raise AttnError(f"{n} must be a one-element float32 GPU tensor")
+        out.append(t.data_ptr())
+    return out
+
+
+def _fp8_out(q, out, lse, lse_shape, out_dtype, return_lse):
+    if out_dtype not in DTYPE_CODES:
+        raise AttnError("out_dtype must be torch.bfloat16 or torch.float16")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _device_tensor(out, "out")
+    if out.shape != q.shape or out.dtype != out_dtype:
+        raise AttnError("out must have q's shape and out_dtype")
+    if lse is None and return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_like(lse, torch.empty(lse_shape, device="meta"), "lse", torch.float32)
+    return out, lse
+
+
+def attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 descale_q: torch.Tensor | None = None, descale_k: torch.Tensor | None = None,
+                 descale_v: torch.Tensor | None = None, causal: bool = False,
+                 window_left: int = -1, window_right: int = -1,
+                 softmax_scale: float | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                 return_lse: bool = True):
+    """FP8 forward: q [B, Hq, N, 128], k, v [B, Hkv, N, 128] as E4M3 codes; descales are
+    one-element fp32 GPU tensors or None (= 1).  Returns (o in out_dtype, lse fp32)."""
+    _fp8_inputs(q, k, v, 4)
+    bsz, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (bsz, n, d):
+        raise AttnError("k, v must match q in batch, sequence length and head dim")
+    scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d))
+    dq, dk, dv = _descales(descale_q, descale_k, descale_v)
+    out, lse = _fp8_out(q, out, lse, (bsz, hq, n), out_dtype, return_lse)
+    lib = load_library()
+    st = lib.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, dq, dk, dv, bsz, hq,
+                          hkv, n, d, DTYPE_CODES[out_dtype], scale, int(bool(causal)),
+                          int(window_left), int(window_right), _stream_handle(q.device))
+    _check(st, "attn_fwd_fp8")
+    return out, lse
+
+
+def attn_fwd_varlen_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        cu_seqlens: torch.Tensor, max_seqlen: int,
+                        descale_q: torch.Tensor | None = None,
+                        descale_k: torch.Tensor | None = None,
+                        descale_v: torch.Tensor | None = None, causal: bool = False,
+                        window_left: int = -1, window_right: int = -1,
+                        softmax_scale: float | None = None,
+                        out_dtype: torch.dtype = torch.bfloat16,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                        return_lse: bool = True):
+    """Packed FP8 forward: q [Hq, total, 128], k, v [Hkv, total, 128] E4M3 codes."""
+    _fp8_inputs(q, k, v, 3)
+    _device_tensor(cu_seqlens, "cu_seqlens")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise AttnError("cu_seqlens must be a 1-D int32 tensor of num_seqs + 1 entries")
+    hq, total, d = q.shape
+    hkv = k.shape[0]
+    if (k.shape[1], k.shape[2]) != (total, d):
+        raise AttnError("k, v must match q in total tokens and head dim")
+    scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(d))
+    dq, dk, dv = _descales(descale_q, descale_k, descale_v)
+    out, lse = _fp8_out(q, out, lse, (hq, total), out_dtype, return_lse)
+    lib = load_library()
+    st = lib.attn_fwd_varlen_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, dq, dk, dv,
+                                 cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen),
+                                 total, hq, hkv, d, DTYPE_CODES[out_dtype], scale,
+                                 int(bool(causal)), int(window_left), int(window_right),
+                                 _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen_fp8")
+    return out, lse

@@ -7,6 +7,7 @@
 
 #include "exact_attn.h"
 #include "attn_bwd.h"
+#include "attn_fwd_fp8.h"
 #include "attn_dispatch.h"
 
 namespace xattn {
@@ -352,6 +353,25 @@ int run_bwd(const Plan& p, int head_dim, int dtype, long slots, long heads_q, lo
   return hip_status(xattn::launch_bwd<128>(b, bf16, p.mode, (int)n_q, (int)n_k, s));
 }
 
+// ---- FP8 forward -------------------------------------------------------------------------
+
+int run_fp8(Plan& p, long slots, long heads, long outer, const float* dq, const float* dk,
+            const float* dv, int out_dtype, void* stream) {
+  if ((dq && !aligned(dq, 4)) || (dk && !aligned(dk, 4)) || (dv && !aligned(dv, 4)))
+    return ATTN_ERR_MISALIGNED;
+  const long n_work = outer * heads * slots;
+  if (slots > std::numeric_limits<int>::max() || n_work > std::numeric_limits<int>::max())
+    return ATTN_ERR_TOO_LARGE;
+  xattn::Fp8Args f{};
+  f.f = p.a;
+  f.f.tiles_per_head = (int)slots;
+  f.descale_q = dq;
+  f.descale_k = dk;
+  f.descale_v = dv;
+  return hip_status(xattn::launch_fwd_fp8(f, out_dtype == ATTN_DTYPE_BF16, p.mode, (int)n_work,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -472,6 +492,37 @@ int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o
   return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const float* descale_q, const float* descale_k, const float* descale_v,
+                 int batch, int heads_q, int heads_kv, int seqlen, int head_dim, int out_dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream) {
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen, head_dim, out_dtype,
+                      softmax_scale, causal, window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const long slots = ((long)seqlen + xattn::Fp8Shape::BR - 1) / xattn::Fp8Shape::BR;
+  return run_fp8(p, slots, heads_q, batch, descale_q, descale_k, descale_v, out_dtype, stream);
+}
+
+int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* descale_q, const float* descale_k,
+                        const float* descale_v, const int32_t* cu_seqlens, int num_seqs,
+                        int max_seqlen, int total_tokens, int heads_q, int heads_kv,
+                        int head_dim, int out_dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream) {
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
+                       heads_q, heads_kv, head_dim, out_dtype, softmax_scale, causal,
+                       window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  constexpr int B = xattn::Fp8Shape::BR;
+  const long by_total = ((long)total_tokens + B - 1) / B + num_seqs;
+  const long by_max = (long)num_seqs * ((max_seqlen + B - 1) / B);
+  return run_fp8(p, by_total < by_max ? by_total : by_max, heads_q, 1, descale_q, descale_k,
+                 descale_v, out_dtype, stream);
+}
+
 size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen) {
   if (batch <= 0 || heads_q <= 0 || seqlen <= 0) return 0;
   return bwd_workspace_bytes((long)batch * heads_q * seqlen);
@@ -523,7 +574,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
     case ATTN_ERR_UNSUPPORTED_HEAD_DIM:
       return "ATTN_ERR_UNSUPPORTED_HEAD_DIM: head_dim must be 64, 128, 256 or 512 (backward: "
-             "64 or 128)";
+             "64 or 128; FP8: 128)";
     case ATTN_ERR_UNSUPPORTED_DTYPE:
       return "ATTN_ERR_UNSUPPORTED_DTYPE: dtype must be ATTN_DTYPE_FP16 or ATTN_DTYPE_BF16";
     case ATTN_ERR_MISALIGNED:

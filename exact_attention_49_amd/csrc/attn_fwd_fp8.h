@@ -1,0 +1,310 @@
+// FP8 (E4M3) exact-attention forward for gfx950, head_dim 128: Q, K, V are 8-bit floats with
+// one fp32 descale per tensor; O is written in bf16 or fp16 with the natural-log LSE.
+//
+// What is computed: plain attention of the dequantized tensors (code * descale).  As on the
+// pages, the Q and K descales fold into the softmax scale and the V descale is applied to the
+// output (page "flash_fwd_kernel.h" @c272619, `compute_attn_ws_fp8`; page "flash_fwd_kernel.h"
+// @26a6e0a: a missing scale pointer means 1), and P is exponentiated with an offset of 8 in the
+// exponent (`Max_offset`), so that its largest values use the upper part of the E4M3 range
+// (P in (0, 256]) before it is rounded to E4M3 for the P V product.
+//
+// MFMA: v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3), 32 bytes of A and of B per lane.  The
+// products pair A and B bytes by the same (lane half, byte) -> k rule, so loading both
+// operands of S^T = K Q^T as 32 contiguous bytes of a row needs no knowledge of that rule.
+// For O^T += V^T P^T the two operands are built differently (P from registers, V^T with
+// ds_read_b64_tr_b8), so both are laid out by one explicit key order: byte b of lane half hh
+// is key 32 (b / 16) + 16 hh + b % 16 of the 64-key tile.
+//  * So that the S^T accumulators come out in that order, K rows sit in LDS in a permuted slot
+//    order: slot i of a 32-key block holds key perm(i) = 16 ((i >> 2) & 1) + 4 (i >> 3) + i % 4.
+//    Lane l reads slot l % 32 as its A row, and accumulator register r of lane half hh then
+//    holds key 32 kb + 16 hh + r.
+//  * ds_read_b64_tr_b8 (measured on gfx950): a group of 16 lanes reads an 8-row x 16-byte block
+//    (lane i gives row i / 2, bytes 8 (i % 2) .. + 7) and lane i receives column i of the block,
+//    rows 0..7 as bytes 0..7.  Four such reads give a lane the 32 keys of its P bytes for one
+//    column d of V.
+// K and V tiles are stored with 128-byte rows and the 16-byte chunk index XOR (row / 2) % 8,
+// which spreads the row reads of K and the transpose reads of V over all banks.
+#pragma once
+
+#include "attn_common.h"
+
+namespace xattn {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct Fp8Args {
+  FwdArgs f;                 // q, k, v hold E4M3 codes; o is bf16 / fp16
+  const float* descale_q;    // null = 1
+  const float* descale_k;
+  const float* descale_v;
+};
+
+struct Fp8Shape {
+  static constexpr int NW = 4, NT = 256, BR = 128, BC = 64, WPE = 2;
+};
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // format 0 (E4M3) for both operands, no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Four fp32 values -> four E4M3 bytes (round to nearest even) in one dword.
+__device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// LDS slot of key kk (0..31) of a 32-key block: the inverse of perm above.
+__device__ __forceinline__ int key_slot(int kk) {
+  return 8 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
+}
+
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+}
+
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(Fp8Shape::NT) __attribute__((amdgpu_waves_per_eu(Fp8Shape::WPE)))
+void attn_fwd_fp8_kernel(Fp8Args fa) {
+  constexpr int D = 128;
+  const FwdArgs& a = fa.f;
+  constexpr int BC = Fp8Shape::BC, NT = Fp8Shape::NT, BR = Fp8Shape::BR;
+  constexpr int CH = D / 16;            // 16-byte chunks per row
+  constexpr int TILEB = BC * D;         // bytes per K (or V) tile
+  constexpr int LPT = BC * CH / NT;     // chunks per thread per matrix per tile
+  static_assert(BC * CH % NT == 0 && BC == 64, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  Work w;
+  if (!decode_work<BR, MODE>(a, w)) return;
+  const int seqlen = w.seqlen;
+  int wl, wr;
+  mode_windows<MODE>(a, wl, wr);
+
+  const int q0 = w.tile * BR;
+  const int qw0 = q0 + wave * 32;
+  const int q_last = min(q0 + BR, seqlen) - 1;
+  int k_lo = 0, k_hi = seqlen - 1;
+  if (wl >= 0) k_lo = max(0, q0 - wl);
+  if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
+  const int t_lo = k_lo / BC, t_hi = k_hi / BC;
+
+  const bool wave_active = qw0 < seqlen;
+  const int qw_last = min(qw0 + 32, seqlen) - 1;
+  int kw_lo = 0, kw_hi = seqlen - 1;
+  if (wl >= 0) kw_lo = max(0, qw0 - wl);
+  if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
+
+  const uint8_t* __restrict__ kp = (const uint8_t*)a.k + w.kv_row0 * D;
+  const uint8_t* __restrict__ vp = (const uint8_t*)a.v + w.kv_row0 * D;
+  const int qrow = qw0 + l32;
+
+  // Q^T operand: lane's query row, bytes 64 c + 32 hh .. + 31 of d-chunk c
+  i32x8 qf[D / 64];
+  {
+    const uint8_t* src = (const uint8_t*)a.q + (w.row0 + qrow) * D;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      i32x4 lo4 = {0, 0, 0, 0}, hi4 = {0, 0, 0, 0};
+      if (qrow < seqlen) {
+        lo4 = *(const i32x4*)(src + 64 * c + 32 * hh);
+        hi4 = *(const i32x4*)(src + 64 * c + 32 * hh + 16);
+      }
+      qf[c] = (i32x8){lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    }
+  }
+  const float dsq = fa.descale_q ? *fa.descale_q : 1.f;
+  const float dsk = fa.descale_k ? *fa.descale_k : 1.f;
+  const float dsv = fa.descale_v ? *fa.descale_v : 1.f;
+  const float c2 = a.scale_log2 * dsq * dsk;
+  constexpr float OFFSET = 8.0f;  // P = 2^(s - m + 8) in (0, 256]
+
+  // per-lane LDS byte offsets: K row reads (slot l32, chunks 4c + 2hh and + 1, swizzled) and
+  // V transpose reads (row 16 hh + i16 / 2, bytes 32 db + 16 (g & 1) + 8 (i16 & 1))
+  int kofs[D / 64][2];
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      kofs[c][h2] = l32 * D + (((4 * c + 2 * hh + h2) ^ swz8(l32)) << 4);
+  // (row + 32 has the swizzle key of row; row + 8 and row + 40 that of row + 8)
+  const int g = lane >> 4, i16 = lane & 15;
+  const int vrow = 16 * hh + (i16 >> 1);
+  int vofs[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = 32 * db + 16 * (g & 1) + 8 * (i16 & 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = vrow + 8 * e;
+      vofs[db][e] = row * D + (((col >> 4) ^ swz8(row)) << 4) + (col & 15);
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  i32x4 stage_k[LPT], stage_v[LPT];
+  auto gload = [&](int t) {
+    const int kbase = t * BC;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      const int key = kbase + r;
+      if (key < seqlen) {
+        stage_k[u] = *(const i32x4*)(kp + (long)key * D + 16 * c);
+        stage_v[u] = *(const i32x4*)(vp + (long)key * D + 16 * c);
+      } else {
+        stage_k[u] = (i32x4){0, 0, 0, 0};
+        stage_v[u] = (i32x4){0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int s) {
+    char* kt = smem + s * 2 * TILEB;
+    char* vt = kt + TILEB;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int id = tid + u * NT;
+      const int r = id / CH, c = id % CH;
+      const int slot = (r & ~31) + key_slot(r & 31);
+      *(i32x4*)(kt + slot * D + ((c ^ swz8(slot)) << 4)) = stage_k[u];
+      *(i32x4*)(vt + r * D + ((c ^ swz8(r)) << 4)) = stage_v[u];
+    }
+  };
+
+  auto consume = [&](int t, int s) {
+    const int k0 = t * BC;
+    if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;
+    const char* kt = smem + s * 2 * TILEB;
+    const char* vt = kt + TILEB;
+    // S^T = K Q^T: register r of block kb, lane half hh holds key k0 + 32 kb + 16 hh + r
+    f32x16 sacc[BC / 32];
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) {
+        const char* base = kt + kb * 32 * D;
+        const i32x4 x0 = *(const i32x4*)(base + kofs[c][0]);
+        const i32x4 x1 = *(const i32x4*)(base + kofs[c][1]);
+        const i32x8 av = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        sacc[kb] = mfma_fp8(av, qf[c], sacc[kb]);
+      }
+    }
+    // mask: key offset 32 kb + 16 hh + r against the row's visible range
+    const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
+                           (wl >= 0 && k0 < qw0 + 31 - wl);
+    if (need_mask) {
+      const int base = k0 + 16 * hh;
+      int lo = wl >= 0 ? qrow - wl - base : -(1 << 30);
+      int hi = seqlen - 1 - base;
+      if (wr >= 0) hi = min(hi, qrow + wr - base);
+      if (lo > hi) lo = hi = -(1 << 30);
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + r;
+          if (min(max(c, lo), hi) != c) sacc[kb][r] = -INFINITY;
+        }
+    }
+    // softmax with the exact running max and the exponent offset
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = halves_max(mx) * c2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new - OFFSET;
+    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+    const bool moved = m_new > m_run;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(sacc[kb][r], c2, -m_use));
+        sacc[kb][r] = e;
+        ps += e;
+      }
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // wave-uniform
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run *= alpha;
+    }
+    l_run += ps;
+    m_run = m_new;
+    // P^T operand: bytes 16 kb + r <- register r of block kb (key 32 kb + 16 hh + r)
+    i32x8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kb = j >> 2, r0 = 4 * (j & 3);
+      pf[j] = pack4_fp8(sacc[kb][r0], sacc[kb][r0 + 1], sacc[kb][r0 + 2], sacc[kb][r0 + 3]);
+    }
+    // O^T += V^T P^T: column d = 32 db + l32, keys in the same byte order via four
+    // transpose reads (rows 16 hh + 0..7, + 8..15, + 32..39, + 40..47)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const i32x2 r0 = lds_read_tr8(vt + vofs[db][0]);
+      const i32x2 r1 = lds_read_tr8(vt + vofs[db][1]);
+      const i32x2 r2 = lds_read_tr8(vt + vofs[db][0] + 32 * D);
+      const i32x2 r3 = lds_read_tr8(vt + vofs[db][1] + 32 * D);
+      const i32x8 av = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+      oacc[db] = mfma_fp8(av, pf, oacc[db]);
+    }
+  };
+
+  gload(t_lo);
+  lstore(0);
+  __syncthreads();
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int s = (t - t_lo) & 1;
+    if (t < t_hi) gload(t + 1);
+    consume(t, s);
+    if (t < t_hi) lstore(s ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  // epilogue: O = O * descale_v / l, LSE = (m - 8 + log2 l) ln 2
+  constexpr float LN2 = 0.693147180559945309f;
+  const float lt = halves_sum(l_run);
+  if (qrow >= seqlen) return;
+  const float inv = lt > 0.f ? dsv / lt : 0.f;
+  uint16_t* dst = a.o + (w.row0 + qrow) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& x = oacc[db];
+      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
+                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
+      *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
+    }
+  if (a.lse != nullptr && hh == 0)
+    a.lse[w.row0 + qrow] = lt > 0.f ? (m_run - OFFSET + fast_log2(lt)) * LN2 : -INFINITY;
+}
+
+// Host launcher (defined in attn_fwd_fp8.hip): out_bf16 selects the output type.
+hipError_t launch_fwd_fp8(const Fp8Args& a, bool out_bf16, int mode, int n_work,
+                          hipStream_t stream);
+
+}  // namespace xattn

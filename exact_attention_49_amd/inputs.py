@@ -19,7 +19,7 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_dense", "make_varlen", "make_workload",
-           "make_upstream"]
+           "make_upstream", "quantize_fp8"]
 
 _DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
@@ -49,6 +49,7 @@ class Workload:
     heads_kv: int = 0       # key/value heads (grouped-query attention); 0: as many as `heads`
     splitkv: bool = False   # run through the split-KV entry point
     backward: bool = False  # time the backward pass (dO drawn with seed + 100)
+    fp8: bool = False       # E4M3 inputs (drawn as `dtype`, then quantize_fp8 per tensor)
     note: str = field(default="", compare=False)
 
     @property
@@ -97,6 +98,11 @@ WORKLOADS = {
                  seqlen=8192, head_dim=128, dtype="bf16", causal=True, seed=4907,
                  value_scale=0.5,
                  note="B=2 Hq=32 Hkv=8 N=8192 d=128 bf16 causal, inputs N(0,1)*0.5"),
+        # the FP8 forward on the forward benchmark's shape (bf16 output)
+        Workload("fp8_causal_d128_n8192", batch=2, heads=32, seqlen=8192, head_dim=128,
+                 dtype="bf16", causal=True, seed=4908, fp8=True,
+                 note="B=2 H=32 N=8192 d=128 causal, E4M3 Q/K/V with per-tensor descales, "
+                      "bf16 O"),
         # the backward pass on the forward benchmark's shape
         Workload("bwd_causal_bf16_d128_n8192", batch=2, heads=32, seqlen=8192, head_dim=128,
                  dtype="bf16", causal=True, seed=4903, value_scale=0.5, backward=True,
@@ -161,3 +167,17 @@ def make_upstream(shape, dtype: str, seed: int, value_scale: float = 1.0):
     if value_scale != 1.0:
         x = x * value_scale
     return x.to(_DTYPES[dtype])
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-tensor E4M3 quantisation of an input: descale = amax / 448 (as fp32) and codes =
+    x / descale cast to torch.float8_e4m3fn (round to nearest even).  Returns (codes,
+    descale); the codes stand for codes * descale."""
+    x = x.float()
+    descale = float(torch.tensor(float(x.abs().max()) / E4M3_MAX, dtype=torch.float32))
+    if descale == 0.0:
+        descale = 1.0
+    return (x / descale).to(torch.float8_e4m3fn), descale

@@ -52,7 +52,7 @@ enum {
 enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,          /* null pointer, bad size, scale or mask argument      */
-  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 2, /* head_dim not in {64, 128, 256, 512} (bwd: 64, 128)  */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 2, /* head_dim not supported by the call (see each call)  */
   ATTN_ERR_UNSUPPORTED_DTYPE = 3,    /* dtype not fp16 / bf16                               */
   ATTN_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte or lse/cu_seqlens not 4-byte    */
   ATTN_ERR_TOO_LARGE = 5,            /* a size would overflow the kernel's index arithmetic */
@@ -163,6 +163,34 @@ size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int 
 int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim);
 int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
                                        int heads, int head_dim);
+
+/*
+ * FP8 forward: q, k, v hold 8-bit E4M3 codes (the OCP format: 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite value 448), one byte per element, in the layouts of
+ * attn_fwd_gqa / attn_fwd_varlen_gqa.  Each tensor stands for code * descale, with one fp32
+ * descale per tensor given as a DEVICE pointer (NULL = 1, 4-byte aligned otherwise).  The
+ * result is attention of the dequantized tensors: the Q and K descales fold into the softmax
+ * scale and the V descale multiplies the output (page "flash_fwd_kernel.h" @c272619,
+ * `compute_attn_ws_fp8`: descale_q, descale_k, descale_v; page "flash_fwd_kernel.h" @26a6e0a:
+ * a missing scale pointer means 1).  P is rounded to E4M3 for the P V product, exponentiated
+ * with the pages' offset of 8 (`Max_offset`) so that it spans (0, 256].
+ *   o         : bf16 or fp16 output (out_dtype = ATTN_DTYPE_BF16 / ATTN_DTYPE_FP16), laid out
+ *               as q with 2-byte elements; lse as in the forward (may be NULL).
+ *   head_dim  : 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ * Everything else (masks, heads, errors, stream) is as for attn_fwd_gqa / attn_fwd_varlen_gqa.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 const float* descale_q, const float* descale_k, const float* descale_v,
+                 int batch, int heads_q, int heads_kv, int seqlen, int head_dim, int out_dtype,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 void* stream);
+
+int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* descale_q, const float* descale_k,
+                        const float* descale_v, const int32_t* cu_seqlens, int num_seqs,
+                        int max_seqlen, int total_tokens, int heads_q, int heads_kv,
+                        int head_dim, int out_dtype, float softmax_scale, int causal,
+                        int window_left, int window_right, void* stream);
 
 /*
  * Backward pass: the gradients dQ, dK, dV of a loss L given dO = dL/dO, for the forward that

@@ -294,3 +294,28 @@ def test_bwd_empty_problem_is_a_no_op(lib):
     assert call_bwd(lib, b=0, ws=None, wsb=0) == 0
     assert call_bwd_varlen(lib, ns=0, ws=None, wsb=0) == 0
     assert call_bwd(lib, b=0, d=256) == 2   # non-size arguments are still checked
+
+
+# ---- FP8 forward (host-side validation only) -------------------------------------------------
+
+def call_fp8(lib, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=None, dq=None, dk=None, dv=None, b=1, hq=2, hkv=1,
+                n=256, d=128, out=1, scale=SCALE, causal=1, wl=-1, wr=-1)
+    args.update(kw)
+    return lib.attn_fwd_fp8(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dq"],
+                            args["dk"], args["dv"], args["b"], args["hq"], args["hkv"], args["n"],
+                            args["d"], args["out"], args["scale"], args["causal"], args["wl"],
+                            args["wr"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(d=64), 2), (dict(d=256), 2), (dict(out=2), 3),
+    (dict(q=A + 8), 4), (dict(o=A + 2), 4), (dict(dq=A + 2), 4), (dict(dv=A + 1), 4),
+    (dict(hq=4, hkv=3), 1), (dict(scale=0.0), 1), (dict(wl=-3), 1),
+])
+def test_fp8_rejects_bad_arguments(lib, kw, status):
+    assert call_fp8(lib, **kw) == status
+
+
+def test_fp8_empty_problem_is_a_no_op(lib):
+    assert call_fp8(lib, b=0, q=None, k=None, v=None, o=None) == 0
