@@ -22,8 +22,11 @@
 //    (lane i gives row i / 2, bytes 8 (i % 2) .. + 7) and lane i receives column i of the block,
 //    rows 0..7 as bytes 0..7.  Four such reads give a lane the 32 keys of its P bytes for one
 //    column d of V.
-// K and V tiles are stored with 128-byte rows and the 16-byte chunk index XOR (row / 2) % 8,
-// which spreads the row reads of K and the transpose reads of V over all banks.
+// K and V tiles are stored with 128-byte rows and the 16-byte chunk index XORed with a
+// function of the row, so that neither the K row reads nor the V transpose reads hit a bank
+// twice: K uses (row / 2) % 8 (16 lanes read rows 2i, 2i + 1 of one chunk); V uses
+// 2 ((row / 2) % 4), because a transpose read serves 32 lanes at a time, two 16-lane groups
+// reading adjacent chunks of the same 8 rows.
 #pragma once
 
 #include "attn_common.h"
@@ -55,6 +58,7 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
 }
 
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz8v(int row) { return ((row >> 1) & 3) << 1; }
 
 // LDS slot of key kk (0..31) of a 32-key block: the inverse of perm above.
 __device__ __forceinline__ int key_slot(int kk) {
@@ -135,7 +139,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
       kofs[c][h2] = l32 * D + (((4 * c + 2 * hh + h2) ^ swz8(l32)) << 4);
-  // (row + 32 has the swizzle key of row; row + 8 and row + 40 that of row + 8)
+  // (rows + 32 share the swizzle key of row, rows + 40 that of row + 8)
   const int g = lane >> 4, i16 = lane & 15;
   const int vrow = 16 * hh + (i16 >> 1);
   int vofs[D / 32][2];
@@ -145,7 +149,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int row = vrow + 8 * e;
-      vofs[db][e] = row * D + (((col >> 4) ^ swz8(row)) << 4) + (col & 15);
+      vofs[db][e] = row * D + (((col >> 4) ^ swz8v(row)) << 4) + (col & 15);
     }
   }
 
@@ -182,7 +186,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
       const int r = id / CH, c = id % CH;
       const int slot = (r & ~31) + key_slot(r & 31);
       *(i32x4*)(kt + slot * D + ((c ^ swz8(slot)) << 4)) = stage_k[u];
-      *(i32x4*)(vt + r * D + ((c ^ swz8(r)) << 4)) = stage_v[u];
+      *(i32x4*)(vt + r * D + ((c ^ swz8v(r)) << 4)) = stage_v[u];
     }
   };
 
