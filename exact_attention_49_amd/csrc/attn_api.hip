@@ -306,12 +306,11 @@ int run_split(Plan& p, int head_dim, int dtype, int num_splits, void* workspace,
 
 bool bwd_head_dim(int d) { return d == 64 || d == 128; }
 
-// Q-tile (= key-tile) slots per head of the backward kernels for a packed batch: an upper
-// bound on sum_s ceil(len_s / 128) that needs no lengths.
-long bwd_varlen_slots(int num_seqs, int max_seqlen, int total_tokens) {
-  constexpr int B = xattn::BwdShape::BR;
-  const long by_total = ((long)total_tokens + B - 1) / B + num_seqs;
-  const long by_max = (long)num_seqs * ((max_seqlen + B - 1) / B);
+// Tile slots per head of `rows`-row tiles for a packed batch: an upper bound on
+// sum_s ceil(len_s / rows) that needs no lengths.
+long varlen_slots(int rows, int num_seqs, int max_seqlen, int total_tokens) {
+  const long by_total = ((long)total_tokens + rows - 1) / rows + num_seqs;
+  const long by_max = (long)num_seqs * ((max_seqlen + rows - 1) / rows);
   return by_total < by_max ? by_total : by_max;
 }
 
@@ -325,21 +324,23 @@ int check_bwd_pointers(const float* lse, const void* dout, void* dq, void* dk, v
   return ATTN_OK;
 }
 
-// Launch both backward kernels for a validated plan: `slots` q-tiles (= key tiles) per head,
-// over heads_q query heads and heads_q / kv_group key/value heads.
-int run_bwd(const Plan& p, int head_dim, int dtype, long slots, long heads_q, long outer,
-            const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace,
-            size_t workspace_size, void* stream) {
+// Launch both backward kernels for a validated plan: q_slots q-tiles per query head (dQ
+// kernel) and k_slots key tiles per key/value head (dK/dV kernel), over heads_q query heads
+// and heads_q / kv_group key/value heads.
+int run_bwd(const Plan& p, int head_dim, int dtype, long q_slots, long k_slots, long heads_q,
+            long outer, const void* dout, void* dq, void* dk, void* dv, float scale,
+            void* workspace, size_t workspace_size, void* stream) {
   if (!workspace || !aligned(workspace, 256) || workspace_size < bwd_workspace_bytes(p.rows))
     return ATTN_ERR_INVALID_ARG;
-  const long n_q = outer * heads_q * slots;
-  const long n_k = outer * (heads_q / p.a.kv_group) * slots;
-  if (slots > std::numeric_limits<int>::max() || n_q > std::numeric_limits<int>::max())
+  const long n_q = outer * heads_q * q_slots;
+  const long n_k = outer * (heads_q / p.a.kv_group) * k_slots;
+  constexpr long kIntMax = std::numeric_limits<int>::max();
+  if (q_slots > kIntMax || k_slots > kIntMax || n_q > kIntMax || n_k > kIntMax)
     return ATTN_ERR_TOO_LARGE;
   xattn::BwdArgs b{};
   b.f = p.a;
-  b.f.tiles_per_head = (int)slots;
-  b.ktiles_per_head = (int)slots;
+  b.f.tiles_per_head = (int)q_slots;
+  b.ktiles_per_head = (int)k_slots;
   b.dout = static_cast<const uint16_t*>(dout);
   b.dq = static_cast<uint16_t*>(dq);
   b.dk = static_cast<uint16_t*>(dk);
@@ -516,11 +517,8 @@ int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, fl
                        heads_q, heads_kv, head_dim, out_dtype, softmax_scale, causal,
                        window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  constexpr int B = xattn::Fp8Shape::BR;
-  const long by_total = ((long)total_tokens + B - 1) / B + num_seqs;
-  const long by_max = (long)num_seqs * ((max_seqlen + B - 1) / B);
-  return run_fp8(p, by_total < by_max ? by_total : by_max, heads_q, 1, descale_q, descale_k,
-                 descale_v, out_dtype, stream);
+  return run_fp8(p, varlen_slots(xattn::Fp8Shape::BR, num_seqs, max_seqlen, total_tokens),
+                 heads_q, 1, descale_q, descale_k, descale_v, out_dtype, stream);
 }
 
 size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen) {
@@ -545,9 +543,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (p.status != ATTN_OK || p.empty) return p.status;
   const int st = check_bwd_pointers(lse, dout, dq, dk, dv);
   if (st != ATTN_OK) return st;
-  const long slots = ((long)seqlen + xattn::BwdShape::BR - 1) / xattn::BwdShape::BR;
-  return run_bwd(p, head_dim, dtype, slots, heads_q, batch, dout, dq, dk, dv, softmax_scale,
-                 workspace, workspace_size, stream);
+  const long q_slots = ((long)seqlen + xattn::BwdShape::BR - 1) / xattn::BwdShape::BR;
+  const long k_slots = ((long)seqlen + xattn::BwdShape::BK - 1) / xattn::BwdShape::BK;
+  return run_bwd(p, head_dim, dtype, q_slots, k_slots, heads_q, batch, dout, dq, dk, dv,
+                 softmax_scale, workspace, workspace_size, stream);
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
@@ -563,9 +562,10 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
   if (p.status != ATTN_OK || p.empty) return p.status;
   const int st = check_bwd_pointers(lse, dout, dq, dk, dv);
   if (st != ATTN_OK) return st;
-  return run_bwd(p, head_dim, dtype, bwd_varlen_slots(num_seqs, max_seqlen, total_tokens),
-                 heads_q, 1, dout, dq, dk, dv, softmax_scale, workspace, workspace_size,
-                 stream);
+  return run_bwd(p, head_dim, dtype,
+                 varlen_slots(xattn::BwdShape::BR, num_seqs, max_seqlen, total_tokens),
+                 varlen_slots(xattn::BwdShape::BK, num_seqs, max_seqlen, total_tokens), heads_q,
+                 1, dout, dq, dk, dv, softmax_scale, workspace, workspace_size, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -36,15 +36,20 @@ struct BwdArgs {
   uint16_t* dv;            // laid out as v
   float* dpsum;            // [rows of q]: written by the dQ kernel, read by the dK/dV kernel
   float scale;             // softmax scale (dQ and dK are multiplied by it)
-  int ktiles_per_head;     // key-tile slots per key/value head (dK/dV kernel)
+  int ktiles_per_head;     // key-tile slots per key/value head (dK/dV kernel); the q-tile
+                           // slots of the dQ kernel are f.tiles_per_head
 };
 
 struct BwdShape {
+  // dQ kernel: DQ_NW waves of 32 query rows share each K/V tile of BC keys, DQ_WPE waves per
+  // SIMD
+  static constexpr int DQ_NW = 8, DQ_NT = 64 * DQ_NW, DQ_WPE = 2;
+  static constexpr int BR = 32 * DQ_NW;  // query rows per workgroup
+  static constexpr int BC = 64;          // keys per K/V tile
+  // dK/dV kernel: 4 waves of 32 keys, Q/dO tiles of BQ rows
   static constexpr int NW = 4, NT = 256;
-  static constexpr int BR = 128;   // dQ kernel: query rows per workgroup
-  static constexpr int BC = 64;    // dQ kernel: keys per K/V tile
-  static constexpr int BK = 128;   // dK/dV kernel: keys per workgroup
-  static constexpr int BQ = 64;    // dK/dV kernel: query rows per Q/dO tile
+  static constexpr int BK = 128;         // keys per workgroup
+  static constexpr int BQ = 64;          // query rows per Q/dO tile
 };
 
 // Sum of the eight products of two packed 16-bit vectors, in fp32.
@@ -106,10 +111,11 @@ __device__ __forceinline__ float lse_to_log2(float lse) {
 // ---------------------------------------------------------------------------------------------
 
 template <bool BF16, int D, int MODE>
-__global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(BwdShape::DQ_NT)
+__attribute__((amdgpu_waves_per_eu(BwdShape::DQ_WPE)))
 void attn_bwd_dq_kernel(BwdArgs ba) {
   const FwdArgs& a = ba.f;
-  constexpr int BR = BwdShape::BR, BC = BwdShape::BC, NT = BwdShape::NT;
+  constexpr int BR = BwdShape::BR, BC = BwdShape::BC, NT = BwdShape::DQ_NT;
   constexpr int CH = D / 8, ROWB = D * 2, TILEB = BC * ROWB, LPT = BC * CH / NT;
   constexpr int STAGEB = 3 * TILEB;  // K (row-read swizzle), K (transpose swizzle), V
   static_assert(BC * CH % NT == 0, "tile must split evenly over the threads");
@@ -452,8 +458,8 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, int mode, int n_q, int n_k,
 
 template <bool BF16, int D, int MODE>
 hipError_t launch_bwd_mode(const BwdArgs& a, int n_q, int n_k, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, MODE>), dim3(n_q), dim3(BwdShape::NT), 0, s,
-                     a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, MODE>), dim3(n_q), dim3(BwdShape::DQ_NT), 0,
+                     s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, MODE>), dim3(n_k), dim3(BwdShape::NT), 0,
