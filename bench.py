@@ -375,6 +375,12 @@ def main() -> int:
 
     flops = workload_flops(w, cu)
     algo_bytes = workload_bytes(w, cu)
+    # the device as the HIP runtime reports it: the published peak assumes 256 CUs at 2.4 GHz
+    # and 4096 dense 16-bit MFMA flops per clock per CU (twice that for FP8)
+    from exact_attention_49_amd.binding import device_info
+    dev_info = device_info(0)
+    clock_peak = (dev_info["compute_units"] * dev_info["clock_mhz"] * 1e6
+                  * (8192 if w.fp8 else 4096) / 1e12)
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS["fp8" if w.fp8 else w.dtype]
@@ -416,6 +422,8 @@ def main() -> int:
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
         "kernel_source_hash": kernel_source_hash(w.backward),
+        "device": {**dev_info, "peak_tflops_at_reported_clock": round(clock_peak, 1),
+                   "pct_of_clock_peak": round(100 * value / clock_peak, 2)},
     }
     if cold is not None:
         out["cold_cache"] = cold

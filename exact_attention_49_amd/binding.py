@@ -58,6 +58,7 @@ EXPORTED_SYMBOLS = {
     "attn_bwd_varlen": (_I, [_P] * 10 + [_I] * 7 + [_F] + [_I] * 3 + [_P, _S, _P]),
     "attn_bwd_workspace_size": (_S, [_I, _I, _I]),
     "attn_bwd_varlen_workspace_size": (_S, [_I, _I]),
+    "attn_device_info": (_I, [_I, _P, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
 }
@@ -505,3 +506,12 @@ def attn_fwd_varlen_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  _stream_handle(q.device))
     _check(st, "attn_fwd_varlen_fp8")
     return out, lse
+
+
+def device_info(device: int = 0) -> dict:
+    """Compute units and peak engine clock (MHz) of a HIP device, from the HIP runtime."""
+    lib = load_library()
+    cus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.attn_device_info(int(device), ctypes.byref(cus), ctypes.byref(clk)),
+           "attn_device_info")
+    return {"compute_units": cus.value, "clock_mhz": clk.value / 1000.0}

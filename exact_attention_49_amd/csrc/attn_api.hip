@@ -568,6 +568,17 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                  1, dout, dq, dk, dv, softmax_scale, workspace, workspace_size, stream);
 }
 
+int attn_device_info(int device, int* num_cus, int* clock_khz) {
+  if (!num_cus || !clock_khz) return ATTN_ERR_INVALID_ARG;
+  int cus = 0, clk = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, device);
+  if (e != hipSuccess) return hip_status(e);
+  *num_cus = cus;
+  *clock_khz = clk;
+  return ATTN_OK;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK: success";

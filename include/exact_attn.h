@@ -23,8 +23,9 @@
  *     causal must be 0 or 1; window_left/window_right are >= 0, or -1 for unbounded.
  *     causal = 1 is the window mask with window_right = 0.
  *   - stream is a hipStream_t (NULL = the null stream).  Calls are asynchronous: they only
- *     enqueue kernels.  The library allocates no memory and keeps no state except a cached
- *     device query, so concurrent calls from several threads are safe.
+ *     enqueue kernels.  The library allocates no memory and keeps no state except the
+ *     calling thread's last HIP error code, so concurrent calls from several threads are
+ *     safe.
  *   - Errors are returned, never thrown or printed; nothing is launched when the arguments
  *     fail validation.  Arguments are validated on the host only: the contents of device
  *     arrays (cu_seqlens) are trusted.
@@ -230,6 +231,11 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
 /* Workspace bytes of a backward call (0 for an empty problem).  Host-only. */
 size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen);
 size_t attn_bwd_varlen_workspace_size(int total_tokens, int heads_q);
+
+/* Compute units and peak engine clock (kHz) of HIP device `device`, as the HIP runtime
+ * reports them (host-only query, for sizing and reporting; the kernels do not depend on it).
+ * ATTN_ERR_INVALID_ARG on null pointers, ATTN_ERR_HIP if the runtime query fails. */
+int attn_device_info(int device, int* num_cus, int* clock_khz);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

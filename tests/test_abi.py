@@ -319,3 +319,7 @@ def test_fp8_rejects_bad_arguments(lib, kw, status):
 
 def test_fp8_empty_problem_is_a_no_op(lib):
     assert call_fp8(lib, b=0, q=None, k=None, v=None, o=None) == 0
+
+
+def test_device_info_rejects_null_pointers(lib):
+    assert lib.attn_device_info(0, None, None) == 1
