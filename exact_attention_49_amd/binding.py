@@ -456,8 +456,9 @@ def attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  softmax_scale: float | None = None, out_dtype: torch.dtype = torch.bfloat16,
                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                  return_lse: bool = True):
-    """FP8 forward: q [B, Hq, N, 128], k, v [B, Hkv, N, 128] as E4M3 codes; descales are
-    one-element fp32 GPU tensors or None (= 1).  Returns (o in out_dtype, lse fp32)."""
+    """FP8 forward: q [B, Hq, N, d], k, v [B, Hkv, N, d] as E4M3 codes (d = 64, 128 or 256);
+    descales are one-element fp32 GPU tensors or None (= 1).  Returns (o in out_dtype, lse
+    fp32)."""
     _fp8_inputs(q, k, v, 4)
     bsz, hq, n, d = q.shape
     hkv = k.shape[1]
@@ -485,7 +486,7 @@ def attn_fwd_varlen_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                         out_dtype: torch.dtype = torch.bfloat16,
                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                         return_lse: bool = True):
-    """Packed FP8 forward: q [Hq, total, 128], k, v [Hkv, total, 128] E4M3 codes."""
+    """Packed FP8 forward: q [Hq, total, d], k, v [Hkv, total, d] E4M3 codes."""
     _fp8_inputs(q, k, v, 3)
     _device_tensor(cu_seqlens, "cu_seqlens")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:

@@ -356,8 +356,10 @@ int run_bwd(const Plan& p, int head_dim, int dtype, long q_slots, long k_slots, 
 
 // ---- FP8 forward -------------------------------------------------------------------------
 
-int run_fp8(Plan& p, long slots, long heads, long outer, const float* dq, const float* dk,
-            const float* dv, int out_dtype, void* stream) {
+bool fp8_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+int run_fp8(Plan& p, int head_dim, long slots, long heads, long outer, const float* dq,
+            const float* dk, const float* dv, int out_dtype, void* stream) {
   if ((dq && !aligned(dq, 4)) || (dk && !aligned(dk, 4)) || (dv && !aligned(dv, 4)))
     return ATTN_ERR_MISALIGNED;
   const long n_work = outer * heads * slots;
@@ -369,8 +371,8 @@ int run_fp8(Plan& p, long slots, long heads, long outer, const float* dq, const 
   f.descale_q = dq;
   f.descale_k = dk;
   f.descale_v = dv;
-  return hip_status(xattn::launch_fwd_fp8(f, out_dtype == ATTN_DTYPE_BF16, p.mode, (int)n_work,
-                                          reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(xattn::launch_fwd_fp8(f, head_dim, out_dtype == ATTN_DTYPE_BF16, p.mode,
+                                          (int)n_work, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -498,12 +500,13 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int batch, int heads_q, int heads_kv, int seqlen, int head_dim, int out_dtype,
                  float softmax_scale, int causal, int window_left, int window_right,
                  void* stream) {
-  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!fp8_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   Plan p = plan_dense(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen, head_dim, out_dtype,
                       softmax_scale, causal, window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
   const long slots = ((long)seqlen + xattn::Fp8Shape::BR - 1) / xattn::Fp8Shape::BR;
-  return run_fp8(p, slots, heads_q, batch, descale_q, descale_k, descale_v, out_dtype, stream);
+  return run_fp8(p, head_dim, slots, heads_q, batch, descale_q, descale_k, descale_v, out_dtype,
+                 stream);
 }
 
 int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -512,13 +515,14 @@ int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, fl
                         int max_seqlen, int total_tokens, int heads_q, int heads_kv,
                         int head_dim, int out_dtype, float softmax_scale, int causal,
                         int window_left, int window_right, void* stream) {
-  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!fp8_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
                        heads_q, heads_kv, head_dim, out_dtype, softmax_scale, causal,
                        window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  return run_fp8(p, varlen_slots(xattn::Fp8Shape::BR, num_seqs, max_seqlen, total_tokens),
-                 heads_q, 1, descale_q, descale_k, descale_v, out_dtype, stream);
+  return run_fp8(p, head_dim,
+                 varlen_slots(xattn::Fp8Shape::BR, num_seqs, max_seqlen, total_tokens), heads_q,
+                 1, descale_q, descale_k, descale_v, out_dtype, stream);
 }
 
 size_t attn_bwd_workspace_size(int batch, int heads_q, int seqlen) {
@@ -585,7 +589,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
     case ATTN_ERR_UNSUPPORTED_HEAD_DIM:
       return "ATTN_ERR_UNSUPPORTED_HEAD_DIM: head_dim must be 64, 128, 256 or 512 (backward: "
-             "64 or 128; FP8: 128)";
+             "64 or 128; FP8: 64, 128 or 256)";
     case ATTN_ERR_UNSUPPORTED_DTYPE:
       return "ATTN_ERR_UNSUPPORTED_DTYPE: dtype must be ATTN_DTYPE_FP16 or ATTN_DTYPE_BF16";
     case ATTN_ERR_MISALIGNED:

@@ -1,4 +1,4 @@
-// FP8 (E4M3) exact-attention forward for gfx950, head_dim 128: Q, K, V are 8-bit floats with
+// FP8 (E4M3) exact-attention forward for gfx950, head_dim 64/128/256: Q, K, V are 8-bit floats with
 // one fp32 descale per tensor; O is written in bf16 or fp16 with the natural-log LSE.
 //
 // What is computed: plain attention of the dequantized tensors (code * descale).  As on the
@@ -22,11 +22,14 @@
 //    (lane i gives row i / 2, bytes 8 (i % 2) .. + 7) and lane i receives column i of the block,
 //    rows 0..7 as bytes 0..7.  Four such reads give a lane the 32 keys of its P bytes for one
 //    column d of V.
-// K and V tiles are stored with 128-byte rows and the 16-byte chunk index XORed with a
-// function of the row, so that neither the K row reads nor the V transpose reads hit a bank
-// twice: K uses (row / 2) % 8 (16 lanes read rows 2i, 2i + 1 of one chunk); V uses
-// 2 ((row / 2) % 4), because a transpose read serves 32 lanes at a time, two 16-lane groups
-// reading adjacent chunks of the same 8 rows.
+// K and V tiles are stored with D-byte rows and the 16-byte chunk index XORed with a function
+// of the row, so that neither the K row reads (16 lanes, 16 consecutive slots, one chunk) nor
+// the V transpose reads (32 lanes: two 16-lane groups reading adjacent chunks of the same 8
+// rows) hit a bank twice.  With 64 four-byte banks, D = 64 / 128 / 256 puts 4 / 2 / 1 rows in
+// one 256-byte bank line, so the keys are:
+//     K:  (slot / 4) % 4,       (slot / 2) % 8,       slot % 16
+//     V:  2 ((row / 4) % 2),    2 ((row / 2) % 4),    2 (row % 8)
+// (rows r and r + 8 share the V key in all three cases).
 #pragma once
 
 #include "attn_common.h"
@@ -43,7 +46,8 @@ struct Fp8Args {
 };
 
 struct Fp8Shape {
-  static constexpr int NW = 4, NT = 256, BR = 128, BC = 64, WPE = 2;
+  static constexpr int NW = 4, NT = 256, BR = 128, BC = 64;
+  template <int D> static constexpr int WPE = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -57,8 +61,12 @@ __device__ __forceinline__ int pack4_fp8(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz8v(int row) { return ((row >> 1) & 3) << 1; }
+template <int D> __device__ __forceinline__ int swz8k(int slot) {
+  return D == 64 ? (slot >> 2) & 3 : D == 128 ? (slot >> 1) & 7 : slot & 15;
+}
+template <int D> __device__ __forceinline__ int swz8v(int row) {
+  return D == 64 ? ((row >> 2) & 1) << 1 : D == 128 ? ((row >> 1) & 3) << 1 : (row & 7) << 1;
+}
 
 // LDS slot of key kk (0..31) of a 32-key block: the inverse of perm above.
 __device__ __forceinline__ int key_slot(int kk) {
@@ -70,10 +78,11 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
 }
 
-template <bool BF16, int MODE>
-__global__ __launch_bounds__(Fp8Shape::NT) __attribute__((amdgpu_waves_per_eu(Fp8Shape::WPE)))
+template <bool BF16, int D, int MODE>
+__global__ __launch_bounds__(Fp8Shape::NT)
+__attribute__((amdgpu_waves_per_eu(Fp8Shape::WPE<D>)))
 void attn_fwd_fp8_kernel(Fp8Args fa) {
-  constexpr int D = 128;
+  static_assert(D == 64 || D == 128 || D == 256, "FP8 head dims");
   const FwdArgs& a = fa.f;
   constexpr int BC = Fp8Shape::BC, NT = Fp8Shape::NT, BR = Fp8Shape::BR;
   constexpr int CH = D / 16;            // 16-byte chunks per row
@@ -138,19 +147,16 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   for (int c = 0; c < D / 64; ++c)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
-      kofs[c][h2] = l32 * D + (((4 * c + 2 * hh + h2) ^ swz8(l32)) << 4);
-  // (rows + 32 share the swizzle key of row, rows + 40 that of row + 8)
+      kofs[c][h2] = l32 * D + (((4 * c + 2 * hh + h2) ^ swz8k<D>(l32)) << 4);
+  // (the V key of a row repeats every 8 rows, so the reads of rows + 8, + 32, + 40 are the
+  // first one's address plus a constant)
   const int g = lane >> 4, i16 = lane & 15;
   const int vrow = 16 * hh + (i16 >> 1);
-  int vofs[D / 32][2];
+  int vofs[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int col = 32 * db + 16 * (g & 1) + 8 * (i16 & 1);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int row = vrow + 8 * e;
-      vofs[db][e] = row * D + (((col >> 4) ^ swz8v(row)) << 4) + (col & 15);
-    }
+    vofs[db] = vrow * D + (((col >> 4) ^ swz8v<D>(vrow)) << 4) + (col & 15);
   }
 
   f32x16 oacc[D / 32];
@@ -185,8 +191,8 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
       const int id = tid + u * NT;
       const int r = id / CH, c = id % CH;
       const int slot = (r & ~31) + key_slot(r & 31);
-      *(i32x4*)(kt + slot * D + ((c ^ swz8(slot)) << 4)) = stage_k[u];
-      *(i32x4*)(vt + r * D + ((c ^ swz8v(r)) << 4)) = stage_v[u];
+      *(i32x4*)(kt + slot * D + ((c ^ swz8k<D>(slot)) << 4)) = stage_k[u];
+      *(i32x4*)(vt + r * D + ((c ^ swz8v<D>(r)) << 4)) = stage_v[u];
     }
   };
 
@@ -267,10 +273,10 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
     // transpose reads (rows 16 hh + 0..7, + 8..15, + 32..39, + 40..47)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const i32x2 r0 = lds_read_tr8(vt + vofs[db][0]);
-      const i32x2 r1 = lds_read_tr8(vt + vofs[db][1]);
-      const i32x2 r2 = lds_read_tr8(vt + vofs[db][0] + 32 * D);
-      const i32x2 r3 = lds_read_tr8(vt + vofs[db][1] + 32 * D);
+      const i32x2 r0 = lds_read_tr8(vt + vofs[db]);
+      const i32x2 r1 = lds_read_tr8(vt + vofs[db] + 8 * D);
+      const i32x2 r2 = lds_read_tr8(vt + vofs[db] + 32 * D);
+      const i32x2 r3 = lds_read_tr8(vt + vofs[db] + 40 * D);
       const i32x8 av = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       oacc[db] = mfma_fp8(av, pf, oacc[db]);
     }
@@ -308,7 +314,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
 }
 
 // Host launcher (defined in attn_fwd_fp8.hip): out_bf16 selects the output type.
-hipError_t launch_fwd_fp8(const Fp8Args& a, bool out_bf16, int mode, int n_work,
+hipError_t launch_fwd_fp8(const Fp8Args& a, int head_dim, bool out_bf16, int mode, int n_work,
                           hipStream_t stream);
 
 }  // namespace xattn

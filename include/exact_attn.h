@@ -177,7 +177,7 @@ int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_t
  * with the pages' offset of 8 (`Max_offset`) so that it spans (0, 256].
  *   o         : bf16 or fp16 output (out_dtype = ATTN_DTYPE_BF16 / ATTN_DTYPE_FP16), laid out
  *               as q with 2-byte elements; lse as in the forward (may be NULL).
- *   head_dim  : 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ *   head_dim  : 64, 128 or 256 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
  * Everything else (masks, heads, errors, stream) is as for attn_fwd_gqa / attn_fwd_varlen_gqa.
  */
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

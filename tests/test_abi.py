@@ -309,7 +309,7 @@ def call_fp8(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(o=None), 1), (dict(d=64), 2), (dict(d=256), 2), (dict(out=2), 3),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(d=96), 2), (dict(d=512), 2), (dict(out=2), 3),
     (dict(q=A + 8), 4), (dict(o=A + 2), 4), (dict(dq=A + 2), 4), (dict(dv=A + 1), 4),
     (dict(hq=4, hkv=3), 1), (dict(scale=0.0), 1), (dict(wl=-3), 1),
 ])

@@ -1,8 +1,10 @@
-"""GPU parity of the FP8 forward (through the C ABI) against the fp64 CPU oracle, which
-attends over the dequantized tensors (code * descale).
+"""GPU parity of the FP8 forward (through the C ABI, head dims 64/128/256) against the fp64
+CPU oracle, which attends over the dequantized tensors (code * descale).
 
-Bars.  The scores are exact products of E4M3 values accumulated in fp32, so the LSE must match
-to 1e-4 * max(1, |LSE|).  O carries the rounding of P to E4M3 before the P V product: a
+Bars.  The LSE is held to the forward's bar, 1e-3 * max(1, |LSE|).  The products of E4M3
+values are exact, but the FP8 MFMA's internal sums are not round-to-nearest fp32: the measured
+score error grows like d * 2^-24 * |S| (8.8e-4 in the LSE of the sharp d = 256 case, where |S|
+reaches about 50), so no tighter bar holds.  O carries the rounding of P to E4M3 before the P V product: a
 relative error of at most 2^-4 for P in the normal range and 2^-10 absolute below it, with P
 scaled so that its row sum is at least 256.  Per element that bounds
     |O_gpu - O_ref| <= 2^-4 * (P|V|)_i + 2^-18 * sum_{j visible} |V_j| + 2^-8 |O_ref| + 1e-6,
@@ -54,12 +56,11 @@ def _check(o, lse, o_ref, lse_ref, bound, what):
     fin = np.isfinite(lse_ref)
     assert np.all(lse[~fin] == -np.inf)
     d = np.abs(lse[fin] - lse_ref[fin])
-    assert np.all(d <= 1e-4 * np.maximum(1.0, np.abs(lse_ref[fin]))), f"{what}: LSE {d.max():.2e}"
+    assert np.all(d <= 1e-3 * np.maximum(1.0, np.abs(lse_ref[fin]))), f"{what}: LSE {d.max():.2e}"
     return float(np.max(err / bound))
 
 
-def _dense_case(bsz, hq, hkv, n, m, seed, value_scale=1.0, out_dtype=torch.bfloat16):
-    d = 128
+def _dense_case(bsz, hq, hkv, n, m, seed, value_scale=1.0, out_dtype=torch.bfloat16, d=128):
     (q8, dq), (k8, dk), (v8, dv) = _quantized((bsz, hq, n, d), (bsz, hkv, n, d), seed,
                                               value_scale)
     dts = [torch.tensor([x], dtype=torch.float32, device=DEV) for x in (dq, dk, dv)]
@@ -85,6 +86,21 @@ def _dense_case(bsz, hq, hkv, n, m, seed, value_scale=1.0, out_dtype=torch.bfloa
 def test_fp8_dense(mask, n):
     _announce(f"fp8 dense n={n} {mask}")
     _dense_case(2, 2, 2, n, MASKS[mask], seed=3100 + n)
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_other_head_dims(d, mask):
+    _announce(f"fp8 d={d} {mask}")
+    _dense_case(2, 2, 2, 300, MASKS[mask], seed=3150 + d, d=d)
+    _dense_case(1, 2, 2, 1025, MASKS[mask], seed=3160 + d, d=d)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_other_head_dims_gqa_and_sharp(d):
+    _announce(f"fp8 d={d} gqa, sharp")
+    _dense_case(1, 6, 2, 257, MASKS["causal"], seed=3170 + d, d=d)
+    _dense_case(1, 2, 2, 400, MASKS["causal"], seed=3180 + d, value_scale=4.0, d=d)
 
 
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 1)])
@@ -123,20 +139,21 @@ def test_fp8_descale_none_means_one():
     assert float(np.max(np.abs(to64(lse) - lse_ref))) <= 1e-3
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("mask", ["causal", "window_30_70"])
-def test_fp8_varlen(mask):
-    _announce(f"fp8 varlen {mask}")
+def test_fp8_varlen(mask, d):
+    _announce(f"fp8 varlen d={d} {mask}")
     m = MASKS[mask]
     lens = [1, 0, 64, 300, 129, 3]
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
     total = int(cu[-1])
-    (q8, dq), (k8, dk), (v8, dv) = _quantized((4, total, 128), (2, total, 128), 3700)
+    (q8, dq), (k8, dk), (v8, dv) = _quantized((4, total, d), (2, total, d), 3700 + d)
     dts = [torch.tensor([x], dtype=torch.float32, device=DEV) for x in (dq, dk, dv)]
     o, lse = attn_fwd_varlen_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), cu.to(DEV), max(lens),
                                  *dts, causal=m["causal"], window_left=m["wl"],
                                  window_right=m["wr"])
     torch.cuda.synchronize()
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     cun = cu.numpy()
     o_ref, lse_ref = ofp8.attention_fp8_varlen(_codes(q8), _codes(k8), _codes(v8), cun, scale,
                                                dq, dk, dv, m["causal"], m["wl"], m["wr"])
