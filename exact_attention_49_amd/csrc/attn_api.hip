@@ -504,7 +504,8 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   Plan p = plan_dense(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen, head_dim, out_dtype,
                       softmax_scale, causal, window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  const long slots = ((long)seqlen + xattn::Fp8Shape::BR - 1) / xattn::Fp8Shape::BR;
+  const int br = xattn::fp8_block_rows(head_dim);
+  const long slots = ((long)seqlen + br - 1) / br;
   return run_fp8(p, head_dim, slots, heads_q, batch, descale_q, descale_k, descale_v, out_dtype,
                  stream);
 }
@@ -521,7 +522,8 @@ int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, fl
                        window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
   return run_fp8(p, head_dim,
-                 varlen_slots(xattn::Fp8Shape::BR, num_seqs, max_seqlen, total_tokens), heads_q,
+                 varlen_slots(xattn::fp8_block_rows(head_dim), num_seqs, max_seqlen,
+                              total_tokens), heads_q,
                  1, descale_q, descale_k, descale_v, out_dtype, stream);
 }
 

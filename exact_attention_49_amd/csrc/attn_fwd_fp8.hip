@@ -5,7 +5,7 @@ namespace xattn {
 
 template <int D>
 static void launch_d(const Fp8Args& a, bool out_bf16, int mode, dim3 grid, hipStream_t s) {
-  const dim3 block(Fp8Shape::NT);
+  const dim3 block(Fp8Shape<D>::NT);
   if (out_bf16) {
     if (mode == MASK_NONE) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, D, MASK_NONE>), grid, block, 0, s, a);
     else if (mode == MASK_CAUSAL) hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, D, MASK_CAUSAL>), grid, block, 0, s, a);
