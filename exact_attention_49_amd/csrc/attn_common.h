@@ -1,6 +1,8 @@
-// Shared pieces of the gfx950 exact-attention forward kernels: argument block, MFMA and
-// conversion wrappers, cross-lane reductions, LDS layout (swizzles), work decoding and the
-// per-tile steps (S^T = K Q^T, mask, online softmax, O^T += V^T P^T, epilogue).
+// Shared pieces of the gfx950 exact-attention kernels (the forward kernels use all of it; the
+// backward and FP8 kernels reuse the argument block, the wrappers, work decoding and the
+// 16-bit operand steps): argument block, MFMA and conversion wrappers, cross-lane reductions,
+// LDS layout (swizzles), work decoding and the per-tile steps (S^T = K Q^T, mask, online
+// softmax, O^T += V^T P^T, epilogue).
 //
 // What is computed.  For every query row i of a (batch, head) or (sequence, head):
 //   S_ij = scale * q_i . k_j   (keys j visible under the causal / sliding-window mask),
