@@ -1,0 +1,79 @@
+"""GPU parity at the largest accepted size: one (sequence, head) whose K/V rows span just under
+2^31 bytes (seqlen * head_dim * 2 < 2^31, the library's limit; one row more is rejected with
+ATTN_ERR_TOO_LARGE, which the CPU ABI tests check).  The kernels address a sequence's rows
+with 32-bit byte offsets, so this is where an overflow would show.  A short causal window
+keeps the work small.
+
+Inputs are drawn on the GPU from a seeded torch generator (8.4 M rows per tensor would take
+long on the host); the rows the oracle needs are copied back, so both sides see the same
+rounded values.  Each sampled row is compared with the oracle's attention over exactly the
+keys it sees, [i - window_left, i]."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_49_amd import attn_fwd, attn_fwd_varlen
+from tests.gpu_helpers import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+D = 128
+N_MAX = (2 ** 31 - 1) // (D * 2)  # 8388607 rows: 2147483392 bytes per head
+WL = 64
+
+
+def _draw(shape, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _check_rows(q, k, v, o, lse, rows, what):
+    scale = 1 / math.sqrt(D)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for r in rows:
+        lo = max(0, r - WL)
+        qs = q[r:r + 1].float().cpu().numpy()
+        ks = k[lo:r + 1].float().cpu().numpy()
+        vs = v[lo:r + 1].float().cpu().numpy()
+        oo, ll = oracle.attention_head(qs, ks, vs, scale)   # every key of the slice is visible
+        ref_o.append(oo[0]), ref_l.append(ll[0])
+        got_o.append(o[r].double().cpu().numpy()), got_l.append(float(lse[r]))
+    assert_close(np.array(got_o), np.array(got_l), np.array(ref_o), np.array(ref_l),
+                 torch.bfloat16, what)
+
+
+def test_largest_dense_sequence():
+    print(f"[case] dense N={N_MAX} d={D} window {WL}", flush=True)
+    q, k, v = (_draw((1, 1, N_MAX, D), s) for s in (71, 72, 73))
+    o, lse = attn_fwd(q, k, v, causal=True, window_left=WL)
+    torch.cuda.synchronize()
+    rows = [0, 1, WL, N_MAX // 2, N_MAX - 257, N_MAX - 256, N_MAX - 2, N_MAX - 1]
+    _check_rows(q[0, 0], k[0, 0], v[0, 0], o[0, 0], lse[0, 0], rows, "largest dense")
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_largest_packed_sequence_among_others():
+    """A packed batch whose last sequence is the largest accepted one, behind two short ones:
+    its rows start at a large token offset in the packed arrays."""
+    lens = [1000, 3, N_MAX]
+    total = sum(lens)
+    print(f"[case] varlen total={total} d={D} window {WL}", flush=True)
+    q, k, v = (_draw((1, total, D), s) for s in (74, 75, 76))
+    cu = torch.tensor([0, 1000, 1003, total], dtype=torch.int32, device=DEV)
+    o, lse = attn_fwd_varlen(q, k, v, cu, N_MAX, causal=True, window_left=WL)
+    torch.cuda.synchronize()
+    base = 1003
+    rows = [0, 1, 70, N_MAX // 3, N_MAX - 1]
+    _check_rows(q[0, base:], k[0, base:], v[0, base:], o[0, base:], lse[0, base:], rows,
+                "largest packed")
+    _check_rows(q[0, :1000], k[0, :1000], v[0, :1000], o[0, :1000], lse[0, :1000], [0, 999],
+                "first packed")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
