@@ -266,8 +266,8 @@ def main() -> int:
             print(f"{name}: {w.note}")
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(work units are independent per head; see the sharding note in DESIGN.md). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (its work "
+              "units, one per (batch | sequence, head), shard over GPUs without any exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.calibrate_copy:

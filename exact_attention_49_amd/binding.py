@@ -86,7 +86,8 @@ def load_library():
         if _LIB is None:
             path = library_path()
             if not os.path.exists(path):
-                raise AttnError(f"HIP library {path} is not built; run __graft_entry__.build()")
+                raise AttnError(f"HIP library {path} is not built; run "
+                                "python -m exact_attention_49_amd.build")
             lib = ctypes.CDLL(path)
             for name, (res, args) in EXPORTED_SYMBOLS.items():
                 fn = getattr(lib, name)

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library in-tree: exact_attention_49_amd/libexact_attn.so.
 
-    python -m exact_attention_49_amd.build        (or __graft_entry__.build())
+    python -m exact_attention_49_amd.build
 
 Each csrc/*.hip file is compiled by hipcc for gfx950 in parallel, then linked into one shared
 library.  Packed-fp32 VALU instructions are disabled for the device code.
