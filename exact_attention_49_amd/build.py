@@ -3,7 +3,8 @@
     python -m exact_attention_49_amd.build
 
 Each csrc/*.hip file is compiled by hipcc for gfx950 in parallel, then linked into one shared
-library.  Packed-fp32 VALU instructions are disabled for the device code.
+library.  Packed-fp32 VALU instructions are disabled for the device code.  The plain-C example
+consumer (examples/c_abi_demo.c) is then compiled against the library with gcc.
 """
 
 from __future__ import annotations
@@ -68,7 +69,24 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_c_demo()
     return LIB
+
+
+C_DEMO_SRC = os.path.join(PKG, "examples", "c_abi_demo.c")
+C_DEMO = os.path.join(PKG, "c_abi_demo")
+
+
+def build_c_demo() -> str:
+    """Compile the plain-C example consumer of the library (gcc, C11) next to the library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", "/opt/rocm/include", C_DEMO_SRC, "-L", PKG, "-lexact_attn",
+           "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib",
+           "-o", C_DEMO]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {C_DEMO_SRC}:\n{r.stderr}")
+    return C_DEMO
 
 
 if __name__ == "__main__":
