@@ -100,7 +100,7 @@ def workload_bytes(w, cu=None) -> float:
 def kernel_name(w, cu=None) -> str:
     """The kernel the library launches for a workload (mirrors the host dispatch: the wide
     kernel for d >= 256, the generic kernel for d = 64, and for d = 128 the ping-pong kernel
-    once the grid of 256-row tiles has at least 1024 workgroups, else the generic one)."""
+    once the grid of 256-row tiles has at least 256 workgroups, else the generic one)."""
     if w.backward:
         return "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel (one step)"
     if w.fp8:
@@ -116,7 +116,7 @@ def kernel_name(w, cu=None) -> str:
         tiles = w.heads * ((int(cu[-1]) + 255) // 256)
     else:
         tiles = w.batch * w.heads * ((w.seqlen + 255) // 256)
-    return "attn_fwd_pp_kernel" if tiles >= 1024 else "attn_fwd_kernel"
+    return "attn_fwd_pp_kernel" if tiles >= 256 else "attn_fwd_kernel"
 
 
 def load_traffic(w):
