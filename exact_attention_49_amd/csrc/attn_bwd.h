@@ -46,9 +46,10 @@ struct BwdShape {
   static constexpr int DQ_NW = 8, DQ_NT = 64 * DQ_NW, DQ_WPE = 2;
   static constexpr int BR = 32 * DQ_NW;  // query rows per workgroup
   static constexpr int BC = 64;          // keys per K/V tile
-  // dK/dV kernel: 4 waves of 32 keys, Q/dO tiles of BQ rows
-  static constexpr int NW = 4, NT = 256;
-  static constexpr int BK = 128;         // keys per workgroup
+  // dK/dV kernel: NW waves, two per block of 32 keys (one accumulates dV, the other dK), WPE
+  // waves per SIMD, Q/dO tiles of BQ rows
+  static constexpr int NW = 8, NT = 64 * NW, WPE = 2;
+  static constexpr int BK = 32 * (NW / 2);  // keys per workgroup
   static constexpr int BQ = 64;          // query rows per Q/dO tile
 };
 
@@ -294,20 +295,27 @@ __device__ __forceinline__ bool decode_key_work(const BwdArgs& ba, KeyWork& w) {
 }
 
 template <bool BF16, int D, int MODE>
-__global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(BwdShape::WPE)))
 void attn_bwd_dkdv_kernel(BwdArgs ba) {
   const FwdArgs& a = ba.f;
   constexpr int BK = BwdShape::BK, BQ = BwdShape::BQ, NT = BwdShape::NT;
+  constexpr int HQ = BQ / 2;  // query rows per step of a dK wave
   constexpr int CH = D / 8, ROWB = D * 2, TILEB = BQ * ROWB, LPT = BQ * CH / NT;
   // per stage: Q (row-read swizzle), Q (transpose swizzle), dO (both), LSE2 and dPsum rows
   constexpr int STAGEB = 4 * TILEB + 2 * BQ * 4;
   static_assert(BQ * CH % NT == 0 && BQ <= NT, "tile must split evenly over the threads");
+  static_assert(BK == 32 * (BwdShape::NW / 2), "each key block has one dV and one dK wave");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  // Waves 0..NW/2-1 accumulate dV and the others dK, for the same blocks of 32 keys.  Waves
+  // w and w + NW/2 share a SIMD, so each SIMD runs one wave of each kind and overlaps the
+  // MFMAs of one with the VALU work of the other.  The dK wave recomputes P (five products
+  // per tile pair instead of four) so that the two share nothing but the staged tiles.
+  const bool dk_wave = wave >= BwdShape::NW / 2;
 
   KeyWork w;
   if (!decode_key_work<BK>(ba, w)) return;
@@ -316,7 +324,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   mode_windows<MODE>(a, wl, wr);
 
   const int k0 = w.tile * BK;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + (wave & (BwdShape::NW / 2 - 1)) * 32;
   const int k_last = min(k0 + BK, seqlen) - 1;
   int q_lo = 0, q_hi = seqlen - 1;  // queries that see any key of the workgroup
   if (wr >= 0) q_lo = max(0, k0 - wr);
@@ -333,18 +341,15 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   const int krow = kw0 + l32;
   i32x4 kf[D / 16], vf[D / 16];
   load_q<D>(a.k + w.kv_row0 * D, krow, seqlen, hh, kf);
-  load_q<D>(a.v + w.kv_row0 * D, krow, seqlen, hh, vf);
+  if (dk_wave) load_q<D>(a.v + w.kv_row0 * D, krow, seqlen, hh, vf);
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   const float c2 = a.scale_log2;
 
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 acc[D / 32];  // dV^T (dV waves) or dK^T / scale (dK waves)
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dkacc[db][r] = 0.f;
-      dvacc[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   i32x4 stage_q[LPT], stage_d[LPT];
   float stage_l = INFINITY, stage_p = 0.f;
@@ -394,43 +399,79 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
     }
   };
 
-  auto consume = [&](int it, int s) {
-    const int j = it / nq;
-    const int qbase = (qt_lo + it - j * nq) * BQ;
-    if (!wave_active || qbase > qw_hi || qbase + BQ - 1 < qw_lo) return;
+  // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the window
+  // bounds exchanged.  Whether rows [q0, q0 + n) need it for the wave's keys:
+  auto needs_mask = [&](int q0, int n) {
+    return (q0 + n > seqlen) || (wr >= 0 && q0 < kw0 + 31 - wr) ||
+           (wl >= 0 && q0 + n - 1 > kw0 + wl);
+  };
+
+  // dV wave: S = Q K^T (lane = key), P, dV^T += dO^T P over the whole q-tile.
+  auto consume_dv = [&](int qbase, int s) {
     const char* qn = smem + s * STAGEB;
-    const char* qt = qn + TILEB;
-    const char* dn = qt + TILEB;
-    const char* dt = dn + TILEB;
+    const char* dt = qn + 3 * TILEB;
     const float* ls = (const float*)(dt + TILEB);
-    f32x16 sacc[BQ / 32], dpacc[BQ / 32];
-    mma_scores<BF16, D, BQ>(qn, lo, kf, sacc);  // S[query, key]: lane = key
-    const bool need_mask = (qbase + BQ > seqlen) || (wr >= 0 && qbase < kw0 + 31 - wr) ||
-                           (wl >= 0 && qbase + BQ - 1 > kw0 + wl);
-    // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the
-    // window bounds exchanged
-    if (need_mask) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
-    mma_scores<BF16, D, BQ>(dn, lo, vf, dpacc);  // dP[query, key]
+    f32x16 sacc[BQ / 32];
+    mma_scores<BF16, D, BQ>(qn, lo, kf, sacc);
+    if (needs_mask(qbase, BQ)) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         // register 4 g4 + i of block qb holds query 32 qb + 8 g4 + 4 hh + i
         const f32x4 l2 = *(const f32x4*)(ls + 32 * qb + 8 * g4 + 4 * hh);
-        const f32x4 dd = *(const f32x4*)(ls + BQ + 32 * qb + 8 * g4 + 4 * hh);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g4 + i;
-          const float p = fast_exp2(fmaf(sacc[qb][r], c2, -l2[i]));
-          sacc[qb][r] = p;
-          dpacc[qb][r] = p * (dpacc[qb][r] - dd[i]);  // dS
-        }
+        for (int i = 0; i < 4; ++i)
+          sacc[qb][4 * g4 + i] = fast_exp2(fmaf(sacc[qb][4 * g4 + i], c2, -l2[i]));
       }
-    i32x4 pf[BQ / 16], dsf[BQ / 16];
+    i32x4 pf[BQ / 16];
     pack_operand<BF16, BQ>(sacc, pf);
-    pack_operand<BF16, BQ>(dpacc, dsf);
-    mma_pv<BF16, D, BQ>(dt, lo, pf, dvacc);   // dV^T += dO^T P
-    mma_pv<BF16, D, BQ>(qt, lo, dsf, dkacc);  // dK^T += Q^T dS
+    mma_pv<BF16, D, BQ>(dt, lo, pf, acc);
+  };
+
+  // dK wave: per half q-tile of HQ rows (fewer live registers), S and dP = dO V^T, then
+  // dS = P (dP - dPsum) and dK^T += Q^T dS.
+  auto consume_dk = [&](int qbase, int s) {
+    const char* qn = smem + s * STAGEB;
+    const char* qt = qn + TILEB;
+    const char* dn = qt + TILEB;
+    const float* ls = (const float*)(dn + 2 * TILEB);
+#pragma unroll
+    for (int h = 0; h < BQ / HQ; ++h) {
+      const int q0 = qbase + h * HQ;
+      if (q0 > qw_hi || q0 + HQ - 1 < qw_lo) continue;
+      f32x16 sacc[HQ / 32], dpacc[HQ / 32];
+      mma_scores<BF16, D, HQ>(qn + h * HQ * ROWB, lo, kf, sacc);
+      if (needs_mask(q0, HQ)) mask_scores<HQ>(sacc, q0, krow, seqlen, wr, wl, hh);
+      mma_scores<BF16, D, HQ>(dn + h * HQ * ROWB, lo, vf, dpacc);
+#pragma unroll
+      for (int qb = 0; qb < HQ / 32; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int row = h * HQ + 32 * qb + 8 * g4 + 4 * hh;
+          const f32x4 l2 = *(const f32x4*)(ls + row);
+          const f32x4 dd = *(const f32x4*)(ls + BQ + row);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            const float p = fast_exp2(fmaf(sacc[qb][r], c2, -l2[i]));
+            dpacc[qb][r] = p * (dpacc[qb][r] - dd[i]);  // dS
+          }
+        }
+      i32x4 dsf[HQ / 16];
+      pack_operand<BF16, HQ>(dpacc, dsf);
+      mma_pv<BF16, D, HQ>(qt + h * HQ * ROWB, lo, dsf, acc);
+    }
+  };
+
+  auto consume = [&](int it, int s) {
+    const int j = it / nq;
+    const int qbase = (qt_lo + it - j * nq) * BQ;
+    if (!wave_active || qbase > qw_hi || qbase + BQ - 1 < qw_lo) return;
+    if (dk_wave)
+      consume_dk(qbase, s);
+    else
+      consume_dv(qbase, s);
   };
 
   gload(0);
@@ -445,8 +486,10 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   }
 
   if (wave_active && krow < seqlen) {
-    store_row<BF16, D>(ba.dk + (w.kv_row0 + krow) * D, dkacc, ba.scale, hh);
-    store_row<BF16, D>(ba.dv + (w.kv_row0 + krow) * D, dvacc, 1.0f, hh);
+    if (dk_wave)
+      store_row<BF16, D>(ba.dk + (w.kv_row0 + krow) * D, acc, ba.scale, hh);
+    else
+      store_row<BF16, D>(ba.dv + (w.kv_row0 + krow) * D, acc, 1.0f, hh);
   }
 }
 
