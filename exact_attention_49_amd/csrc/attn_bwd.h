@@ -213,11 +213,13 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     const char* kt = kn + TILEB;
     const char* vn = kt + TILEB;
     f32x16 sacc[BC / 32], dpacc[BC / 32];
+    __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
     mma_scores<BF16, D, BC>(kn, lo, qf, sacc);
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
     mma_scores<BF16, D, BC>(vn, lo, dof, dpacc);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -227,7 +229,9 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
       }
     i32x4 dsf[BC / 16];
     pack_operand<BF16, BC>(sacc, dsf);
+    __builtin_amdgcn_s_setprio(1);
     mma_pv<BF16, D, BC>(kt, lo, dsf, dqacc);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   gload(t_lo);
@@ -412,7 +416,9 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
     const char* dt = qn + 3 * TILEB;
     const float* ls = (const float*)(dt + TILEB);
     f32x16 sacc[BQ / 32];
+    __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
     mma_scores<BF16, D, BQ>(qn, lo, kf, sacc);
+    __builtin_amdgcn_s_setprio(0);
     if (needs_mask(qbase, BQ)) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb)
@@ -426,7 +432,9 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
       }
     i32x4 pf[BQ / 16];
     pack_operand<BF16, BQ>(sacc, pf);
+    __builtin_amdgcn_s_setprio(1);
     mma_pv<BF16, D, BQ>(dt, lo, pf, acc);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // dK wave: per half q-tile of HQ rows (fewer live registers), S and dP = dO V^T, then
@@ -441,9 +449,11 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
       const int q0 = qbase + h * HQ;
       if (q0 > qw_hi || q0 + HQ - 1 < qw_lo) continue;
       f32x16 sacc[HQ / 32], dpacc[HQ / 32];
+      __builtin_amdgcn_s_setprio(1);
       mma_scores<BF16, D, HQ>(qn + h * HQ * ROWB, lo, kf, sacc);
       if (needs_mask(q0, HQ)) mask_scores<HQ>(sacc, q0, krow, seqlen, wr, wl, hh);
       mma_scores<BF16, D, HQ>(dn + h * HQ * ROWB, lo, vf, dpacc);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int qb = 0; qb < HQ / 32; ++qb)
 #pragma unroll
@@ -460,7 +470,9 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
         }
       i32x4 dsf[HQ / 16];
       pack_operand<BF16, HQ>(dpacc, dsf);
+      __builtin_amdgcn_s_setprio(1);
       mma_pv<BF16, D, HQ>(qt + h * HQ * ROWB, lo, dsf, acc);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
