@@ -303,23 +303,29 @@ __global__ __launch_bounds__(BwdShape::NT) __attribute__((amdgpu_waves_per_eu(Bw
 void attn_bwd_dkdv_kernel(BwdArgs ba) {
   const FwdArgs& a = ba.f;
   constexpr int BK = BwdShape::BK, BQ = BwdShape::BQ, NT = BwdShape::NT;
-  constexpr int HQ = BQ / 2;  // query rows per step of a dK wave
   constexpr int CH = D / 8, ROWB = D * 2, TILEB = BQ * ROWB, LPT = BQ * CH / NT;
   // per stage: Q (row-read swizzle), Q (transpose swizzle), dO (both), LSE2 and dPsum rows
   constexpr int STAGEB = 4 * TILEB + 2 * BQ * 4;
+  // P handed from each dV wave to its dK wave: per lane BQ / 2 fp32 scores as fp16
+  constexpr int NPW = BQ / 16;  // 16-byte words per lane
+  constexpr int PBUFB = (BwdShape::NW / 2) * NPW * 64 * 16;
   static_assert(BQ * CH % NT == 0 && BQ <= NT, "tile must split evenly over the threads");
   static_assert(BK == 32 * (BwdShape::NW / 2), "each key block has one dV and one dK wave");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB + PBUFB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  // Waves 0..NW/2-1 accumulate dV and the others dK, for the same blocks of 32 keys.  Waves
-  // w and w + NW/2 share a SIMD, so each SIMD runs one wave of each kind and overlaps the
-  // MFMAs of one with the VALU work of the other.  The dK wave recomputes P (five products
-  // per tile pair instead of four) so that the two share nothing but the staged tiles.
+  // Waves 0..NW/2-1 ("dV waves") and NW/2..NW-1 ("dK waves") take the same blocks of 32 keys;
+  // waves w and w + NW/2 share a SIMD, so each SIMD runs one of each and overlaps the MFMAs of
+  // one with the VALU work of the other.  For q-tile t the dV wave forms S, P and
+  // dV^T += dO^T P, and hands P (as fp16) to its dK wave through LDS.  The dK wave works one
+  // tile behind: dP = dO V^T, dS = P (dP - dPsum) and dK^T += Q^T dS for tile t - 1, whose
+  // staged rows stay in LDS until the second barrier of step t.
+  const int pair = wave & (BwdShape::NW / 2 - 1);
   const bool dk_wave = wave >= BwdShape::NW / 2;
+  i32x4* pbuf = (i32x4*)(smem + 2 * STAGEB) + pair * NPW * 64 + lane;  // word c at [c * 64]
 
   KeyWork w;
   if (!decode_key_work<BK>(ba, w)) return;
@@ -328,7 +334,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   mode_windows<MODE>(a, wl, wr);
 
   const int k0 = w.tile * BK;
-  const int kw0 = k0 + (wave & (BwdShape::NW / 2 - 1)) * 32;
+  const int kw0 = k0 + pair * 32;
   const int k_last = min(k0 + BK, seqlen) - 1;
   int q_lo = 0, q_hi = seqlen - 1;  // queries that see any key of the workgroup
   if (wr >= 0) q_lo = max(0, k0 - wr);
@@ -338,14 +344,14 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
 
   const bool wave_active = kw0 < seqlen;
   const int kw_last = min(kw0 + 32, seqlen) - 1;
-  int qw_lo = 0, qw_hi = seqlen - 1;  // queries that see any key of this wave
+  int qw_lo = 0, qw_hi = seqlen - 1;  // queries that see any key of this pair of waves
   if (wr >= 0) qw_lo = max(0, kw0 - wr);
   if (wl >= 0) qw_hi = min(seqlen - 1, kw_last + wl);
 
   const int krow = kw0 + l32;
-  i32x4 kf[D / 16], vf[D / 16];
-  load_q<D>(a.k + w.kv_row0 * D, krow, seqlen, hh, kf);
-  if (dk_wave) load_q<D>(a.v + w.kv_row0 * D, krow, seqlen, hh, vf);
+  // K (dV waves) or V (dK waves) rows of the lane's key
+  i32x4 kvf[D / 16];
+  load_q<D>((dk_wave ? a.v : a.k) + w.kv_row0 * D, krow, seqlen, hh, kvf);
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   const float c2 = a.scale_log2;
 
@@ -357,6 +363,10 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
 
   i32x4 stage_q[LPT], stage_d[LPT];
   float stage_l = INFINITY, stage_p = 0.f;
+  auto tile_base = [&](int it) {
+    const int j = it / nq;
+    return (qt_lo + it - j * nq) * BQ;
+  };
   auto gload = [&](int it) {
     const int j = it / nq;
     const int qbase = (qt_lo + it - j * nq) * BQ;
@@ -402,24 +412,26 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
       ls[BQ + tid] = stage_p;
     }
   };
-
-  // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the window
-  // bounds exchanged.  Whether rows [q0, q0 + n) need it for the wave's keys:
-  auto needs_mask = [&](int q0, int n) {
-    return (q0 + n > seqlen) || (wr >= 0 && q0 < kw0 + 31 - wr) ||
-           (wl >= 0 && q0 + n - 1 > kw0 + wl);
+  // whether the pair's keys see any query of the tile at qbase
+  auto tile_active = [&](int qbase) {
+    return wave_active && qbase <= qw_hi && qbase + BQ - 1 >= qw_lo;
   };
 
-  // dV wave: S = Q K^T (lane = key), P, dV^T += dO^T P over the whole q-tile.
+  // dV wave, tile it (stage s): S = Q K^T (lane = key), P, dV^T += dO^T P; P as fp16 into ph.
+  // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the window
+  // bounds exchanged.
+  i32x4 ph[NPW];
   auto consume_dv = [&](int qbase, int s) {
     const char* qn = smem + s * STAGEB;
     const char* dt = qn + 3 * TILEB;
     const float* ls = (const float*)(dt + TILEB);
     f32x16 sacc[BQ / 32];
     __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
-    mma_scores<BF16, D, BQ>(qn, lo, kf, sacc);
+    mma_scores<BF16, D, BQ>(qn, lo, kvf, sacc);
     __builtin_amdgcn_s_setprio(0);
-    if (needs_mask(qbase, BQ)) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
+    const bool need_mask = (qbase + BQ > seqlen) || (wr >= 0 && qbase < kw0 + 31 - wr) ||
+                           (wl >= 0 && qbase + BQ - 1 > kw0 + wl);
+    if (need_mask) mask_scores<BQ>(sacc, qbase, krow, seqlen, wr, wl, hh);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
@@ -432,58 +444,51 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
       }
     i32x4 pf[BQ / 16];
     pack_operand<BF16, BQ>(sacc, pf);
+    if constexpr (BF16)
+      pack_operand<false, BQ>(sacc, ph);
+    else
+#pragma unroll
+      for (int c = 0; c < NPW; ++c) ph[c] = pf[c];
     __builtin_amdgcn_s_setprio(1);
     mma_pv<BF16, D, BQ>(dt, lo, pf, acc);
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // dK wave: per half q-tile of HQ rows (fewer live registers), S and dP = dO V^T, then
-  // dS = P (dP - dPsum) and dK^T += Q^T dS.
-  auto consume_dk = [&](int qbase, int s) {
+  // dK wave, tile it (stage s, P of the tile in pbuf): dP = dO V^T, dS, dK^T += Q^T dS.
+  auto consume_dk = [&](int s) {
     const char* qn = smem + s * STAGEB;
     const char* qt = qn + TILEB;
     const char* dn = qt + TILEB;
     const float* ls = (const float*)(dn + 2 * TILEB);
+    f32x16 dpacc[BQ / 32];
+    __builtin_amdgcn_s_setprio(1);
+    mma_scores<BF16, D, BQ>(dn, lo, kvf, dpacc);
+    __builtin_amdgcn_s_setprio(0);
+    i32x4 pw[NPW];
 #pragma unroll
-    for (int h = 0; h < BQ / HQ; ++h) {
-      const int q0 = qbase + h * HQ;
-      if (q0 > qw_hi || q0 + HQ - 1 < qw_lo) continue;
-      f32x16 sacc[HQ / 32], dpacc[HQ / 32];
-      __builtin_amdgcn_s_setprio(1);
-      mma_scores<BF16, D, HQ>(qn + h * HQ * ROWB, lo, kf, sacc);
-      if (needs_mask(q0, HQ)) mask_scores<HQ>(sacc, q0, krow, seqlen, wr, wl, hh);
-      mma_scores<BF16, D, HQ>(dn + h * HQ * ROWB, lo, vf, dpacc);
-      __builtin_amdgcn_s_setprio(0);
+    for (int c = 0; c < NPW; ++c) pw[c] = pbuf[c * 64];
 #pragma unroll
-      for (int qb = 0; qb < HQ / 32; ++qb)
+    for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int row = h * HQ + 32 * qb + 8 * g4 + 4 * hh;
-          const f32x4 l2 = *(const f32x4*)(ls + row);
-          const f32x4 dd = *(const f32x4*)(ls + BQ + row);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 dd = *(const f32x4*)(ls + BQ + 32 * qb + 8 * g4 + 4 * hh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            const float p = fast_exp2(fmaf(sacc[qb][r], c2, -l2[i]));
-            dpacc[qb][r] = p * (dpacc[qb][r] - dd[i]);  // dS
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;
+          // element r of block qb sits in word 2 qb + r / 8, 32-bit lane (r % 8) / 2, half r % 2.
+          // (The element is copied out first: clang's __builtin_bit_cast of a vector element
+          // expression reads the vector's first element.)
+          const int wd = pw[2 * qb + (r >> 3)][(r & 7) >> 1];
+          const f16x2 h2 = __builtin_bit_cast(f16x2, wd);
+          const float p = (float)h2[r & 1];
+          dpacc[qb][r] = p * (dpacc[qb][r] - dd[i]);  // dS
         }
-      i32x4 dsf[HQ / 16];
-      pack_operand<BF16, HQ>(dpacc, dsf);
-      __builtin_amdgcn_s_setprio(1);
-      mma_pv<BF16, D, HQ>(qt + h * HQ * ROWB, lo, dsf, acc);
-      __builtin_amdgcn_s_setprio(0);
-    }
-  };
-
-  auto consume = [&](int it, int s) {
-    const int j = it / nq;
-    const int qbase = (qt_lo + it - j * nq) * BQ;
-    if (!wave_active || qbase > qw_hi || qbase + BQ - 1 < qw_lo) return;
-    if (dk_wave)
-      consume_dk(qbase, s);
-    else
-      consume_dv(qbase, s);
+      }
+    i32x4 dsf[BQ / 16];
+    pack_operand<BF16, BQ>(dpacc, dsf);
+    __builtin_amdgcn_s_setprio(1);
+    mma_pv<BF16, D, BQ>(qt, lo, dsf, acc);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   gload(0);
@@ -492,10 +497,20 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   for (int it = 0; it < n_it; ++it) {
     const int s = it & 1;
     if (it + 1 < n_it) gload(it + 1);
-    consume(it, s);
+    const bool act = tile_active(tile_base(it));
+    if (!dk_wave) {
+      if (act) consume_dv(tile_base(it), s);
+    } else if (it >= 1 && tile_active(tile_base(it - 1))) {
+      consume_dk(s ^ 1);
+    }
+    __syncthreads();  // the dK waves are done with stage s ^ 1 and with the P of tile it - 1
+    if (!dk_wave && act)
+#pragma unroll
+      for (int c = 0; c < NPW; ++c) pbuf[c * 64] = ph[c];
     if (it + 1 < n_it) lstore(s ^ 1);
     __syncthreads();
   }
+  if (dk_wave && tile_active(tile_base(n_it - 1))) consume_dk((n_it - 1) & 1);
 
   if (wave_active && krow < seqlen) {
     if (dk_wave)
