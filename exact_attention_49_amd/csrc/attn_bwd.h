@@ -14,12 +14,14 @@
 //    S^T = K Q^T and dP^T = V dO^T (lane = query, as in the forward), dS^T from them, and
 //    dQ^T += K^T dS^T (the forward's O^T += V^T P^T with K in V's place).  It also writes
 //    dPsum for its rows, which the second kernel reads.
-//  * attn_bwd_dkdv_kernel: one workgroup per tile of 128 keys of one key/value head.  Each
-//    wave keeps its 32 key rows of K and V in registers and sweeps the visible q-tiles of every
-//    query head of the group: S = Q K^T and dP = dO V^T (lane = key), then
-//    dV^T += dO^T P and dK^T += Q^T dS.  The same building blocks as the forward, with the
-//    roles of queries and keys exchanged: the mask is the forward's with the window bounds
-//    swapped (key j sees query i iff j - window_right <= i <= j + window_left).
+//  * attn_bwd_dkdv_kernel: one workgroup per tile of 128 keys of one key/value head, two
+//    waves per 32 keys, sweeping the visible q-tiles of every query head of the group.  The
+//    "dV wave" keeps the keys' K rows in registers and forms S = Q K^T (lane = key), P and
+//    dV^T += dO^T P; it hands P to the "dK wave" through LDS.  The dK wave keeps the V rows
+//    and, one q-tile behind, forms dP = dO V^T, dS and dK^T += Q^T dS.  The same building
+//    blocks as the forward, with the roles of queries and keys exchanged: the mask is the
+//    forward's with the window bounds swapped (key j sees query i iff
+//    j - window_right <= i <= j + window_left).
 // Tiles are staged global -> registers -> LDS, double-buffered.  An operand read both row-wise
 // (MFMA A operand) and transposed (ds_read_b64_tr_b16) is stored twice, once per swizzle.
 #pragma once

@@ -142,7 +142,11 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   const float dsk = fa.descale_k ? *fa.descale_k : 1.f;
   const float dsv = fa.descale_v ? *fa.descale_v : 1.f;
   const float c2 = a.scale_log2 * dsq * dsk;
-  constexpr float OFFSET = 8.0f;  // P = 2^(s - m + 8) in (0, 256]
+  constexpr float OFFSET = 8.0f;  // P = 2^(s - m + 8) in (0, 2^(8 + SLACK)]
+  // The reference max m moves only when a row's tile max exceeds it by more than SLACK (log2
+  // units), which spares most O rescales; P then stays below 2^8.5 = 362, inside E4M3's
+  // largest finite value (448).
+  constexpr float SLACK = 0.5f;
 
   // per-lane LDS byte offsets: K row reads (slot l32, chunks 4c + 2hh and + 1, swizzled) and
   // V transpose reads (row 16 hh + i16 / 2, bytes 32 db + 16 (g & 1) + 8 (i16 & 1))
@@ -237,17 +241,18 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
           if (min(max(c, lo), hi) != c) sacc[kb][r] = -INFINITY;
         }
     }
-    // softmax with the exact running max and the exponent offset
-    float mx = -INFINITY;
+    // softmax with a lazily moved reference max and the exponent offset; the row max runs in
+    // four independent chains
+    float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = halves_max(mx) * c2;
-    const float m_new = fmaxf(m_run, mx);
+      for (int r = 0; r < 16; ++r) pm[r % 4] = fmaxf(pm[r % 4], sacc[kb][r]);
+    const float mx = halves_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3]))) * c2;
+    const bool moved = mx > m_run + SLACK;  // false while both are -inf
+    const float m_new = moved ? mx : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new - OFFSET;
     const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-    const bool moved = m_new > m_run;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
