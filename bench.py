@@ -45,16 +45,30 @@ DEFAULT_WORKLOAD = "causal_bf16_d128_n8192"
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash(backward: bool = False) -> str:
-    """Hash of the HIP sources of the forward (or the backward) kernels and the shared host
-    code: recorded HBM counters are only valid for the kernels they were taken on."""
+# The sources that build each kernel family: its device code, the shared device helpers and
+# the host code that sizes its launches.
+KERNEL_SOURCES = {
+    "fwd": ("attn_common.h", "attn_api.hip", "attn_dispatch.h", "attn_fwd_kernel.h",
+            "attn_fwd_pingpong.h", "attn_fwd_wide.h", "attn_merge.h", "attn_fwd_d64.hip",
+            "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d512.hip"),
+    "fp8": ("attn_common.h", "attn_api.hip", "attn_fwd_fp8.h", "attn_fwd_fp8.hip"),
+    "bwd": ("attn_common.h", "attn_api.hip", "attn_bwd.h", "attn_bwd_d64.hip",
+            "attn_bwd_d128.hip"),
+}
+
+
+def kernel_family(w) -> str:
+    return "bwd" if w.backward else ("fp8" if w.fp8 else "fwd")
+
+
+def kernel_source_hash(family: str) -> str:
+    """Hash of the HIP sources of one kernel family (KERNEL_SOURCES): recorded HBM counters
+    are only valid for the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_49_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        shared = f in ("attn_common.h", "attn_api.hip")
-        if f.endswith((".h", ".hip")) and (shared or f.startswith("attn_bwd") == backward):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -132,7 +146,7 @@ def load_traffic(w):
             key, sep, val = line.partition(":")
             if sep:
                 rec[key.strip()] = val.strip()
-    if rec.get("kernel_source_hash") != kernel_source_hash(w.backward):
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_family(w)):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -421,7 +435,7 @@ def main() -> int:
                      "min_launch_ms": round(min_launch_ms, 4),
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
-        "kernel_source_hash": kernel_source_hash(w.backward),
+        "kernel_source_hash": kernel_source_hash(kernel_family(w)),
         "device": {**dev_info, "peak_tflops_at_reported_clock": round(clock_peak, 1),
                    "pct_of_clock_peak": round(100 * value / clock_peak, 2)},
     }

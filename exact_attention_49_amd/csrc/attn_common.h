@@ -232,10 +232,10 @@ struct Work {
 };
 
 // Map this workgroup to (q-tile, head, batch | sequence) and, in split-KV mode, a split.
-// Dense batches: heads of all batch entries in order, q-tiles of a head consecutive (heaviest
-// first for masked modes, whose later q-tiles see more keys).  Packed batches: the q-tile
-// slots of a head walk the sequences in order; slots past the last tile are unused.  Returns
-// false for an unused slot.
+// Dense batches: heads of all batch entries in order with the q-tiles of a head consecutive;
+// masked modes, whose later q-tiles see more keys, instead run each group of heads tile-major,
+// heaviest first.  Packed batches: the q-tile slots of a head walk the sequences in order;
+// slots past the last tile are unused.  Returns false for an unused slot.
 template <int BR, int MODE, bool SPLIT = false>
 __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
   int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -246,7 +246,26 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
   }
   const int per = a.tiles_per_head;
   if (a.cu_seqlens == nullptr) {
-    const int bh = wid / per, t = wid - bh * per;
+    int bh, t;
+    if constexpr (MODE != MASK_NONE) {
+      // Masked q-tiles differ in cost (a causal tile m sees m + 1 key tiles).  The (batch,
+      // head) pairs are cut into groups of G, inside which the order is tile-major, heaviest
+      // first.  G is chosen so that a group holds at least 32 q-tiles (one per CU of an XCD)
+      // but no more pairs than an XCD's share of the grid: with a few tiles per head, a
+      // head-by-head order would start some heads' heaviest tiles last and leave an XCD on a
+      // long tail; with many, one head's tiles already fill the XCD, and all of them stream
+      // the same K/V through its L2 together.
+      const int nbh = (SPLIT ? gridDim.x / a.num_splits : gridDim.x) / per;
+      const int G = min((nbh + 7) / 8, max(1, (32 + per - 1) / per));
+      const int g = wid / (G * per);
+      const int r = wid - g * G * per;
+      const int gsize = min(G, nbh - g * G);  // the last group may be smaller
+      t = r / gsize;
+      bh = g * G + (r - t * gsize);
+    } else {
+      bh = wid / per;
+      t = wid - bh * per;
+    }
     w.tile = (MODE != MASK_NONE) ? per - 1 - t : t;
     w.seqlen = a.seqlen;
     w.row0 = (long)bh * a.seqlen;
