@@ -46,19 +46,28 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 # The sources that build each kernel family: its device code, the shared device helpers and
-# the host code that sizes its launches.
+# the host code that sizes and dispatches its launches.
+_SHARED = ("attn_common.h", "attn_api.hip")
+_FWD_SHARED = _SHARED + ("attn_dispatch.h",)
 KERNEL_SOURCES = {
-    "fwd": ("attn_common.h", "attn_api.hip", "attn_dispatch.h", "attn_fwd_kernel.h",
-            "attn_fwd_pingpong.h", "attn_fwd_wide.h", "attn_merge.h", "attn_fwd_d64.hip",
-            "attn_fwd_d128.hip", "attn_fwd_d256.hip", "attn_fwd_d512.hip"),
-    "fp8": ("attn_common.h", "attn_api.hip", "attn_fwd_fp8.h", "attn_fwd_fp8.hip"),
-    "bwd": ("attn_common.h", "attn_api.hip", "attn_bwd.h", "attn_bwd_d64.hip",
-            "attn_bwd_d128.hip"),
+    "pingpong": _FWD_SHARED + ("attn_fwd_pingpong.h", "attn_fwd_d128.hip"),
+    "generic": _FWD_SHARED + ("attn_fwd_kernel.h", "attn_merge.h", "attn_fwd_d64.hip",
+                              "attn_fwd_d128.hip"),
+    "wide": _FWD_SHARED + ("attn_fwd_wide.h", "attn_merge.h", "attn_fwd_d256.hip",
+                           "attn_fwd_d512.hip"),
+    "fp8": _SHARED + ("attn_fwd_fp8.h", "attn_fwd_fp8.hip"),
+    "bwd": _SHARED + ("attn_bwd.h", "attn_bwd_d64.hip", "attn_bwd_d128.hip"),
 }
 
 
-def kernel_family(w) -> str:
-    return "bwd" if w.backward else ("fp8" if w.fp8 else "fwd")
+def kernel_family(w, cu=None) -> str:
+    """The KERNEL_SOURCES family of the kernel(s) a workload's step launches."""
+    if w.backward or w.fp8:
+        return "bwd" if w.backward else "fp8"
+    name = kernel_name(w, cu)
+    if name.startswith("attn_fwd_wide_kernel"):
+        return "wide"
+    return "pingpong" if name == "attn_fwd_pp_kernel" else "generic"
 
 
 def kernel_source_hash(family: str) -> str:
@@ -133,7 +142,7 @@ def kernel_name(w, cu=None) -> str:
     return "attn_fwd_pp_kernel" if tiles >= 256 else "attn_fwd_kernel"
 
 
-def load_traffic(w):
+def load_traffic(w, cu=None):
     """HBM bytes per launch from committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE,
     scaled by a plain copy's readings), if they were taken on the current kernel sources;
     else None.  The summary holds `key: value` lines."""
@@ -146,7 +155,7 @@ def load_traffic(w):
             key, sep, val = line.partition(":")
             if sep:
                 rec[key.strip()] = val.strip()
-    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_family(w)):
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel_family(w, cu)):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -398,7 +407,7 @@ def main() -> int:
     value = flops * args.steps / wall / 1e12
     achieved = flops / avg_launch_s / 1e12
     peak = PEAK_TFLOPS["fp8" if w.fp8 else w.dtype]
-    traffic = load_traffic(w)
+    traffic = load_traffic(w, cu)
 
     config = {"workload": w.name, "heads": w.heads, "heads_kv": w.kv_heads,
               "head_dim": w.head_dim, "dtype": w.dtype,
@@ -435,7 +444,7 @@ def main() -> int:
                      "min_launch_ms": round(min_launch_ms, 4),
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_hbm_gbs": round(algo_bytes / avg_launch_s / 1e9, 1)},
-        "kernel_source_hash": kernel_source_hash(kernel_family(w)),
+        "kernel_source_hash": kernel_source_hash(kernel_family(w, cu)),
         "device": {**dev_info, "peak_tflops_at_reported_clock": round(clock_peak, 1),
                    "pct_of_clock_peak": round(100 * value / clock_peak, 2)},
     }

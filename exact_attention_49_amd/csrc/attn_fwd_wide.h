@@ -25,6 +25,10 @@ struct WideShape {
   static constexpr int NW = 4, NT = 256, BR = 128, BC = 32;
 };
 
+// LDS operand reads run PFW - 1 MFMAs ahead of their use: with one wave per SIMD nothing else
+// covers the LDS latency (measured on MI355X at d = 512: depth 5 is about 1% faster than 3)
+constexpr int PFW = 5;
+
 // acc += a * b with acc in AGPRs (v_mfma_f32_32x32x16).  The s_nop covers an operand written
 // by a VALU instruction just before; an MFMA that reads its own previous result as the
 // accumulator needs no wait.
@@ -252,7 +256,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
     if (!vis) return;  // nothing visible
     f32x16 sacc[BC / 32];
     if (spread) {
-      mma_scores<BF16, D, BC>(kt, lo, qf, sacc, [&](auto i) XATTN_INLINE {
+      mma_scores<BF16, D, BC, PFW>(kt, lo, qf, sacc, [&](auto i) XATTN_INLINE {
         constexpr int I = decltype(i)::value;
         if constexpr (I % SH == 0) {
           constexpr int L = I / SH;  // K instructions first, then V
@@ -265,7 +269,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
         }
       });
     } else {
-      mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
+      mma_scores<BF16, D, BC, PFW>(kt, lo, qf, sacc);
     }
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
@@ -277,7 +281,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
       agpr_settle(oacc);
       scale_o_agpr(oacc, alpha);
     }
-    mma_pv_agpr<BF16, D, BC>(vt, lo, pf, oacc);
+    mma_pv_agpr<BF16, D, BC, PFW>(vt, lo, pf, oacc);
   };
 
   // ---- sweep: tiles alternate between the two buffers (parity known at compile time) -------
