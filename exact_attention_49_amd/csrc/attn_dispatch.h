@@ -26,9 +26,12 @@ template <class T> struct UseGeneric {
 
 template <int D> struct TileCfg;
 template <> struct TileCfg<64> {
-  // at d = 64 the softmax outweighs the MFMA work, and three independent waves per SIMD
-  // interleave it better than the two-group ping-pong
-  using Big = UseGeneric<Tile<4, 64, 2, 3>>;
+  // at d = 64 the softmax outweighs the MFMA work, and independent waves interleave it better
+  // than the two-group ping-pong.  Direct global -> LDS loads leave no staging registers, so
+  // the kernel fits 128 VGPRs and four waves per SIMD (measured on MI355X, 16 packed sequences
+  // of H = 32, d = 64: 359 -> 320 us against register staging at three waves per SIMD; three
+  // stages at three waves: 338 us; 8-wave workgroups: 334-340 us)
+  using Big = UseGeneric<Tile<4, 64, 2, 4, true>>;
   using Small = Big;
 };
 template <> struct TileCfg<128> {

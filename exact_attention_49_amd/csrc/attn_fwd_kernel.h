@@ -1,7 +1,8 @@
 // Generic exact-attention forward kernel for gfx950: NW waves, each owning 32 query rows of one
-// (batch|sequence, head) for the whole K/V sweep.  K/V tiles of BC keys are staged
-// global -> registers -> LDS with 16-byte accesses; with STAGES = 2 the next tile's global loads
-// are in flight while the current tile is consumed (one barrier per tile).  Only tiles that
+// (batch|sequence, head) for the whole K/V sweep.  K/V tiles of BC keys reach LDS either staged
+// global -> registers -> LDS with 16-byte accesses (STAGES = 2: the next tile's global loads are
+// in flight while the current tile is consumed), or with DMA straight from global memory into
+// LDS (buffer_load ... lds), STAGES - 1 tiles ahead; one barrier per tile.  Only tiles that
 // cross a mask edge or the end of the sequence evaluate the mask, and a wave skips tiles its
 // rows cannot see.  The math per tile is in attn_common.h.
 #pragma once
@@ -10,11 +11,13 @@
 
 namespace xattn {
 
-// Tile shape: NW waves of 32 query rows, BC keys per K/V tile, STAGES LDS buffers, and at least
-// WPE waves per SIMD (which caps the registers per wave at 512 / WPE).
-template <int NW_, int BC_, int STAGES_, int WPE_>
+// Tile shape: NW waves of 32 query rows, BC keys per K/V tile, STAGES LDS buffers, at least
+// WPE waves per SIMD (which caps the registers per wave at 512 / WPE), and DMA for direct
+// global -> LDS tile loads instead of staging through registers.
+template <int NW_, int BC_, int STAGES_, int WPE_, bool DMA_ = false>
 struct Tile {
   static constexpr int NW = NW_, BC = BC_, STAGES = STAGES_, WPE = WPE_;
+  static constexpr bool DMA = DMA_;
   static constexpr int BR = NW * 32;  // query rows per workgroup
   static constexpr int NT = NW * 64;  // threads per workgroup
 };
@@ -33,7 +36,7 @@ void attn_fwd_kernel(FwdArgs a) {
   static_assert(BC * CH % NT == 0, "tile must split evenly over the threads");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char smem[STAGES * 2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * 2 * TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -135,8 +138,69 @@ void attn_fwd_kernel(FwdArgs a) {
     mma_pv<BF16, D, BC>(vt, lo, pf, oacc);
   };
 
+  // ---- C::DMA: direct global -> LDS loads, STAGES - 1 tiles in flight --------------------
+  // Instruction i of wave w fills the 16-byte LDS slots (i * NW + w) * 64 + lane of a tile:
+  // slot p holds row p / CH, chunk (p % CH) ^ swizzle(row).  One instruction round covers
+  // NW * 64 / CH rows, a whole number of swizzle periods, so instruction i reads the bytes of
+  // instruction 0 shifted by i rounds and one per-lane offset serves all of them.
+  constexpr int NW = C::NW;
+  constexpr int RROWS = NW * 64 / CH;  // rows per instruction round
+  static_assert(!C::DMA || RROWS % 16 == 0, "rounds must cover whole swizzle periods");
+  const int drow = (wave * 64 + lane) / CH, dch = (wave * 64 + lane) % CH;
+  const int dvoff_k = drow * ROWB + ((dch ^ swz_k<D>(drow)) << 4);
+  const int dvoff_v = drow * ROWB + ((dch ^ swz_v<D>(drow)) << 4);
+  const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * ROWB);
+  const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * ROWB);
+  const unsigned smem_a = lds_address(smem);
+  auto dma_tile = [&](int t, int s) XATTN_INLINE {
+    const int kbase = t * BC;
+    const unsigned kdst = smem_a + s * 2 * TILEB + wave * 1024, vdst = kdst + TILEB;
+    if (kbase + BC <= seqlen) {
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        buffer_load_lds16_at<I * NW * 1024, I * RROWS * ROWB>(rsrc_k, dvoff_k, kbase * ROWB, kdst);
+        buffer_load_lds16_at<I * NW * 1024, I * RROWS * ROWB>(rsrc_v, dvoff_v, kbase * ROWB, vdst);
+      });
+    } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        const int row = drow + I * RROWS;
+        const int crow = min(row, seqlen - 1 - kbase);
+        buffer_load_lds16_at<I * NW * 1024, 0>(
+            rsrc_k, crow * ROWB + ((dch ^ swz_k<D>(row)) << 4), kbase * ROWB, kdst);
+        buffer_load_lds16_at<I * NW * 1024, 0>(
+            rsrc_v, crow * ROWB + ((dch ^ swz_v<D>(row)) << 4), kbase * ROWB, vdst);
+      });
+    }
+  };
+  // wait for the loads of all but the newest tile (when `newer`, a later tile's 2 * LPT load
+  // instructions may stay outstanding)
+  auto wait_older = [&](bool newer) XATTN_INLINE {
+    if (newer)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory");
+    else
+      wait_vmem();
+  };
+
   // ---- the sweep over K/V tiles ---------------------------------------------------------
-  if constexpr (STAGES == 2) {
+  if constexpr (C::DMA) {
+    static_assert(STAGES == 2 || STAGES == 3, "direct loads keep one or two tiles in flight");
+    constexpr int LEAD = STAGES - 1;
+    if (n_tiles > 0) dma_tile(t_lo, 0);
+    if (LEAD == 2 && n_tiles > 1) dma_tile(t_lo + 1, 1);
+    wait_older(LEAD == 2 && n_tiles > 1);
+    block_barrier();
+    int s = 0;
+    for (int t = t_lo; t <= t_hi; ++t) {
+      // stage (s + LEAD) % STAGES held tile t - 1, free since the last barrier
+      const int sl = s + LEAD < STAGES ? s + LEAD : s + LEAD - STAGES;
+      if (t + LEAD <= t_hi) dma_tile(t + LEAD, sl);
+      consume(t, s);
+      if (t + 1 <= t_hi) wait_older(LEAD == 2 && t + 2 <= t_hi);
+      block_barrier();
+      s = s + 1 < STAGES ? s + 1 : 0;
+    }
+  } else if constexpr (STAGES == 2) {
     if (n_tiles > 0) {
       gload(t_lo);
       lstore(0);

@@ -22,9 +22,12 @@ from tests.gpu_helpers import assert_close
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-D = 128
-N_MAX = (2 ** 31 - 1) // (D * 2)  # 8388607 rows: 2147483392 bytes per head
 WL = 64
+HEAD_DIMS = (64, 128)  # d = 64: 16777215 rows; d = 128: 8388607 rows (2147483392 bytes per head)
+
+
+def n_max(d):
+    return (2 ** 31 - 1) // (d * 2)
 
 
 def _draw(shape, seed):
@@ -33,7 +36,7 @@ def _draw(shape, seed):
 
 
 def _check_rows(q, k, v, o, lse, rows, what):
-    scale = 1 / math.sqrt(D)
+    scale = 1 / math.sqrt(q.shape[-1])
     got_o, got_l, ref_o, ref_l = [], [], [], []
     for r in rows:
         lo = max(0, r - WL)
@@ -47,7 +50,9 @@ def _check_rows(q, k, v, o, lse, rows, what):
                  torch.bfloat16, what)
 
 
-def test_largest_dense_sequence():
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_largest_dense_sequence(D):
+    N_MAX = n_max(D)
     print(f"[case] dense N={N_MAX} d={D} window {WL}", flush=True)
     q, k, v = (_draw((1, 1, N_MAX, D), s) for s in (71, 72, 73))
     o, lse = attn_fwd(q, k, v, causal=True, window_left=WL)
@@ -59,9 +64,11 @@ def test_largest_dense_sequence():
     torch.cuda.empty_cache()
 
 
-def test_largest_packed_sequence_among_others():
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_largest_packed_sequence_among_others(D):
     """A packed batch whose last sequence is the largest accepted one, behind two short ones:
     its rows start at a large token offset in the packed arrays."""
+    N_MAX = n_max(D)
     lens = [1000, 3, N_MAX]
     total = sum(lens)
     print(f"[case] varlen total={total} d={D} window {WL}", flush=True)
