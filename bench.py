@@ -123,7 +123,8 @@ def workload_bytes(w, cu=None) -> float:
 def kernel_name(w, cu=None) -> str:
     """The kernel the library launches for a workload (mirrors the host dispatch: the wide
     kernel for d >= 256, the generic kernel for d = 64, and for d = 128 the ping-pong kernel
-    once the grid of 256-row tiles has at least 256 workgroups, else the generic one)."""
+    once the grid of 256-row tiles has at least 256 workgroups (384 under a causal or window
+    mask), else the generic one)."""
     if w.backward:
         return "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel (one step)"
     if w.fp8:
@@ -137,9 +138,13 @@ def kernel_name(w, cu=None) -> str:
         return "attn_fwd_kernel"
     if w.varlen:
         tiles = w.heads * ((int(cu[-1]) + 255) // 256)
+        longest = int((cu[1:] - cu[:-1]).max())
     else:
         tiles = w.batch * w.heads * ((w.seqlen + 255) // 256)
-    return "attn_fwd_pp_kernel" if tiles >= 256 else "attn_fwd_kernel"
+        longest = w.seqlen
+    # masked unless the windows cover every key (a window as long as the sequence is none)
+    masked = (w.causal or 0 <= w.window_left < longest or 0 <= w.window_right < longest)
+    return "attn_fwd_pp_kernel" if tiles >= (384 if masked else 256) else "attn_fwd_kernel"
 
 
 def load_traffic(w, cu=None):

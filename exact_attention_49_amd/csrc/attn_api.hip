@@ -170,7 +170,7 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   p.mode = mask_mode(causal, seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);
   p.big = shape == 1 &&
-          (long)batch * heads * ((seqlen + br_big - 1) / br_big) >= xattn::BIG_TILE_MIN_WORK;
+          (long)batch * heads * ((seqlen + br_big - 1) / br_big) >= xattn::big_tile_min_work(p.mode);
   const int br = block_rows(head_dim, p.big);
   xattn::FwdArgs& a = p.a;
   a.q = static_cast<const uint16_t*>(q);
@@ -228,7 +228,7 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
   p.mode = mask_mode(causal, max_seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);
   p.big = shape == 1 && (long)heads * (((long)total_tokens + br_big - 1) / br_big) >=
-                            xattn::BIG_TILE_MIN_WORK;
+                            xattn::big_tile_min_work(p.mode);
   const int br = block_rows(head_dim, p.big);
   // q-tile slots per head: an upper bound on sum_s ceil(len_s / br) that needs no lengths
   const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;

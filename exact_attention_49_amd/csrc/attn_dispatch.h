@@ -36,7 +36,10 @@ template <> struct TileCfg<64> {
 };
 template <> struct TileCfg<128> {
   using Big = UsePingPong;
-  using Small = UseGeneric<Tile<4, 64, 2, 2>>;
+  // LDS-DMA loads: the same occupancy as register staging (2 waves per SIMD) with the global
+  // loads off the VALU and the staging registers gone (measured on MI355X: split-KV B1 H2
+  // N16384 causal 290 -> 252 us; B1 H4 N4096 causal 108 -> 89 us)
+  using Small = UseGeneric<Tile<4, 64, 2, 2, true>>;
 };
 template <> struct TileCfg<256> {
   using Big = UseWide;
@@ -47,10 +50,18 @@ template <> struct TileCfg<512> {
   using Small = Big;
 };
 
-// Workgroups the big shape must yield before it is preferred: one per CU on 256 CUs.  Measured
-// on MI355X at d = 128: from 256 workgroups up the ping-pong kernel is 5-21% faster than the
-// generic one; with 128 it is up to 7% slower on some shapes.
+// Workgroups the big shape must yield before it is preferred.  Unmasked: one per CU on 256
+// CUs (measured on MI355X at d = 128: from 256 workgroups up the ping-pong kernel is 4-7%
+// faster than the generic one; with 128 it is up to 7% slower on some shapes).  Masked q-tiles
+// differ in cost, and with about one 256-row tile per CU the heaviest tiles set the time: at
+// 256 causal (B1 H8 N8192) or windowed tiles the generic kernel's 128-row tiles balance better
+// (196 vs 219 us causal, 59 vs 61 us window 1024), while from 384 causal tiles up the
+// ping-pong kernel is again 2-12% faster.
 constexpr long BIG_TILE_MIN_WORK = 256;
+constexpr long BIG_TILE_MIN_WORK_MASKED = 384;
+inline long big_tile_min_work(int mode) {
+  return mode == MASK_NONE ? BIG_TILE_MIN_WORK : BIG_TILE_MIN_WORK_MASKED;
+}
 
 template <bool BF16, int D, int MODE, class S, bool SPLIT> struct Launch;
 template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong, false> {
