@@ -30,6 +30,9 @@
 //     K:  (slot / 4) % 4,       (slot / 2) % 8,       slot % 16
 //     V:  2 ((row / 4) % 2),    2 ((row / 2) % 4),    2 (row % 8)
 // (rows r and r + 8 share the V key in all three cases).
+// The tiles go straight from global memory into LDS (buffer_load ... lds), double-buffered:
+// each lane fetches the row and chunk that its LDS slot holds under the permutation and
+// swizzle, and the next tile's loads are in flight while the current one is consumed.
 #pragma once
 
 #include "attn_common.h"
@@ -45,9 +48,11 @@ struct Fp8Args {
   const float* descale_v;
 };
 
-// Tile shape per head dim: NW waves of 32 query rows share each K/V tile of BC keys; two waves
-// per SIMD.  At d = 256 the registers only allow two waves per SIMD with eight waves in a
-// workgroup (a few values spill), which measured 1.5x faster than four waves at one per SIMD.
+// Tile shape per head dim: NW waves of 32 query rows share each K/V tile of BC keys; at least
+// two waves per SIMD.  At d = 256 the registers only allow two waves per SIMD with eight waves
+// in a workgroup, which measured 1.5x faster than four waves at one per SIMD.  With the tiles
+// loaded straight into LDS (no staging registers) the kernels use 114-121 VGPRs at d = 64,
+// 159-166 at d = 128 (three waves per SIMD) and 248-255 at d = 256, without spills.
 template <int D> struct Fp8Shape {
   static constexpr int NW = D == 256 ? 8 : 4, NT = 64 * NW, BR = 32 * NW, BC = 64, WPE = 2;
 };
@@ -75,6 +80,10 @@ template <int D> __device__ __forceinline__ int swz8v(int row) {
 __device__ __forceinline__ int key_slot(int kk) {
   return 8 * ((kk >> 2) & 3) + 4 * (kk >> 4) + (kk & 3);
 }
+// Key held by LDS slot s (0..31) of a 32-key block (the inverse of key_slot).
+__device__ __forceinline__ int slot_key(int s) {
+  return 16 * ((s >> 2) & 1) + 4 * (s >> 3) + (s & 3);
+}
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
@@ -94,7 +103,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   constexpr int LPT = BC * CH / NT;     // chunks per thread per matrix per tile
   static_assert(BC * CH % NT == 0 && BC == 64, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -174,33 +183,40 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  i32x4 stage_k[LPT], stage_v[LPT];
-  auto gload = [&](int t) {
+  // K/V tiles go straight from global memory into LDS (buffer_load ... lds).  Instruction i of
+  // wave w fills the 16-byte LDS slots (i * NW + w) * 64 + lane: slot p sits at tile row
+  // p / CH, chunk position p % CH, so the lane fetches the global row and chunk that position
+  // holds (K: the key of that slot and the swizzled chunk; V: the swizzled chunk).  One
+  // instruction round covers RROWS rows, a whole number of key-permutation (32) and swizzle
+  // periods, so instruction i reads instruction 0's bytes shifted by i rounds.
+  constexpr int NW = Fp8Shape<D>::NW;
+  constexpr int RROWS = NW * 64 / CH;
+  static_assert(RROWS % 32 == 0, "rounds must cover whole permutation and swizzle periods");
+  const int dpos = (wave * 64 + lane) / CH, dcp = (wave * 64 + lane) % CH;
+  const int dkrow = (dpos & ~31) + slot_key(dpos & 31);
+  const int dkch = dcp ^ swz8k<D>(dpos), dvch = dcp ^ swz8v<D>(dpos);
+  const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * D);
+  const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * D);
+  const unsigned smem_a = lds_address(smem);
+  auto dma_tile = [&](int t, int s) XATTN_INLINE {
     const int kbase = t * BC;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      const int key = kbase + r;
-      if (key < seqlen) {
-        stage_k[u] = *(const i32x4*)(kp + (long)key * D + 16 * c);
-        stage_v[u] = *(const i32x4*)(vp + (long)key * D + 16 * c);
-      } else {
-        stage_k[u] = (i32x4){0, 0, 0, 0};
-        stage_v[u] = (i32x4){0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int s) {
-    char* kt = smem + s * 2 * TILEB;
-    char* vt = kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      const int slot = (r & ~31) + key_slot(r & 31);
-      *(i32x4*)(kt + slot * D + ((c ^ swz8k<D>(slot)) << 4)) = stage_k[u];
-      *(i32x4*)(vt + r * D + ((c ^ swz8v<D>(r)) << 4)) = stage_v[u];
+    const unsigned kdst = smem_a + s * 2 * TILEB + wave * 1024, vdst = kdst + TILEB;
+    if (kbase + BC <= seqlen) {
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        buffer_load_lds16_at<I * NW * 1024, I * RROWS * D>(rsrc_k, dkrow * D + (dkch << 4),
+                                                           kbase * D, kdst);
+        buffer_load_lds16_at<I * NW * 1024, I * RROWS * D>(rsrc_v, dpos * D + (dvch << 4),
+                                                           kbase * D, vdst);
+      });
+    } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        const int kr = min(dkrow + I * RROWS, seqlen - 1 - kbase);
+        const int vr = min(dpos + I * RROWS, seqlen - 1 - kbase);
+        buffer_load_lds16_at<I * NW * 1024, 0>(rsrc_k, kr * D + (dkch << 4), kbase * D, kdst);
+        buffer_load_lds16_at<I * NW * 1024, 0>(rsrc_v, vr * D + (dvch << 4), kbase * D, vdst);
+      });
     }
   };
 
@@ -291,15 +307,15 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
     }
   };
 
-  gload(t_lo);
-  lstore(0);
-  __syncthreads();
+  dma_tile(t_lo, 0);
+  wait_vmem();
+  block_barrier();
   for (int t = t_lo; t <= t_hi; ++t) {
     const int s = (t - t_lo) & 1;
-    if (t < t_hi) gload(t + 1);
+    if (t < t_hi) dma_tile(t + 1, s ^ 1);  // held tile t - 1, free since the last barrier
     consume(t, s);
-    if (t < t_hi) lstore(s ^ 1);
-    __syncthreads();
+    if (t < t_hi) wait_vmem();
+    block_barrier();
   }
 
   if (!wave_active) return;
