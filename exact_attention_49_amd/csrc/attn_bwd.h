@@ -22,8 +22,10 @@
 //    blocks as the forward, with the roles of queries and keys exchanged: the mask is the
 //    forward's with the window bounds swapped (key j sees query i iff
 //    j - window_right <= i <= j + window_left).
-// Tiles are staged global -> registers -> LDS, double-buffered.  An operand read both row-wise
-// (MFMA A operand) and transposed (ds_read_b64_tr_b16) is stored twice, once per swizzle.
+// Tiles are double-buffered in LDS: the dQ kernel loads K and V straight from global memory
+// into LDS (buffer_load ... lds), the dK/dV kernel stages Q, dO, LSE and dPsum through
+// registers.  An operand read both row-wise (MFMA A operand) and transposed
+// (ds_read_b64_tr_b16) is stored twice, once per swizzle.
 #pragma once
 
 #include "attn_common.h"
@@ -123,7 +125,7 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
   constexpr int STAGEB = 3 * TILEB;  // K (row-read swizzle), K (transpose swizzle), V
   static_assert(BC * CH % NT == 0, "tile must split evenly over the threads");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -177,34 +179,43 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-  i32x4 stage_k[LPT], stage_v[LPT];
-  auto gload = [&](int t) {
+  // K/V tiles go straight from global memory into LDS (buffer_load ... lds), K twice (one copy
+  // per read swizzle) and V once.  Instruction i of wave w fills the 16-byte LDS slots
+  // (i * NW + w) * 64 + lane of a tile (row p / CH, chunk position p % CH): the lane fetches
+  // the chunk that position holds.  One instruction round covers RROWS rows, a whole number of
+  // swizzle periods, so instruction i reads instruction 0's bytes shifted by i rounds.
+  constexpr int NW = BwdShape::DQ_NW;
+  constexpr int RROWS = NW * 64 / CH;
+  static_assert(RROWS % 16 == 0, "rounds must cover whole swizzle periods");
+  const int drow = (wave * 64 + lane) / CH, dch = (wave * 64 + lane) % CH;
+  const int doff_n = drow * ROWB + ((dch ^ swz_k<D>(drow)) << 4);
+  const int doff_t = drow * ROWB + ((dch ^ swz_v<D>(drow)) << 4);
+  const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * ROWB);
+  const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * ROWB);
+  const unsigned smem_a = lds_address(smem);
+  auto dma_tile = [&](int t, int s) XATTN_INLINE {
     const int kbase = t * BC;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      const int key = kbase + r;
-      if (key < seqlen) {
-        stage_k[u] = ((const i32x4*)(kp + (long)key * D))[c];
-        stage_v[u] = ((const i32x4*)(vp + (long)key * D))[c];
-      } else {  // past the end: zeros (those keys are masked)
-        stage_k[u] = (i32x4){0, 0, 0, 0};
-        stage_v[u] = (i32x4){0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int s) {
-    char* kn = smem + s * STAGEB;
-    char* kt = kn + TILEB;
-    char* vn = kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      *(i32x4*)(kn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_k[u];
-      *(i32x4*)(kt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_k[u];
-      *(i32x4*)(vn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_v[u];
+    const unsigned knd = smem_a + s * STAGEB + wave * 1024, ktd = knd + TILEB, vnd = ktd + TILEB;
+    if (kbase + BC <= seqlen) {
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        constexpr int L = I * NW * 1024, G = I * RROWS * ROWB;
+        buffer_load_lds16_at<L, G>(rsrc_k, doff_n, kbase * ROWB, knd);
+        buffer_load_lds16_at<L, G>(rsrc_k, doff_t, kbase * ROWB, ktd);
+        buffer_load_lds16_at<L, G>(rsrc_v, doff_n, kbase * ROWB, vnd);
+      });
+    } else {  // last tile: rows past the end re-read the sequence's last row (masked keys)
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        constexpr int L = I * NW * 1024;
+        const int row = drow + I * RROWS;
+        const int crow = min(row, seqlen - 1 - kbase) * ROWB;
+        const int on = crow + ((dch ^ swz_k<D>(row)) << 4);
+        const int ot = crow + ((dch ^ swz_v<D>(row)) << 4);
+        buffer_load_lds16_at<L, 0>(rsrc_k, on, kbase * ROWB, knd);
+        buffer_load_lds16_at<L, 0>(rsrc_k, ot, kbase * ROWB, ktd);
+        buffer_load_lds16_at<L, 0>(rsrc_v, on, kbase * ROWB, vnd);
+      });
     }
   };
 
@@ -236,15 +247,15 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  gload(t_lo);
-  lstore(0);
-  __syncthreads();
+  dma_tile(t_lo, 0);
+  wait_vmem();
+  block_barrier();
   for (int t = t_lo; t <= t_hi; ++t) {
     const int s = (t - t_lo) & 1;
-    if (t < t_hi) gload(t + 1);
+    if (t < t_hi) dma_tile(t + 1, s ^ 1);  // held tile t - 1, free since the last barrier
     consume(t, s);
-    if (t < t_hi) lstore(s ^ 1);
-    __syncthreads();
+    if (t < t_hi) wait_vmem();
+    block_barrier();
   }
 
   if (wave_active && qrow < seqlen) store_row<BF16, D>(ba.dq + grow * D, dqacc, ba.scale, hh);
