@@ -307,7 +307,8 @@ def main() -> int:
     from exact_attention_49_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_gqa,
                                         attn_fwd_splitkv,
                                         attn_fwd_varlen, attn_fwd_varlen_gqa,
-                                        splitkv_num_splits, splitkv_workspace_size)
+                                        splitkv_num_splits, splitkv_workspace_size,
+                                        bwd_workspace_size, varlen_bwd_workspace_size)
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     cu = None
@@ -338,7 +339,9 @@ def main() -> int:
                      window_right=w.window_right, out=od, lse=lsed)
         dod = inputs_upstream(w, q).to(dev)
         dqd, dkd, dvd = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        ws = torch.empty(od.numel() // w.head_dim * 4 + 256, dtype=torch.uint8, device=dev)
+        nbytes = (varlen_bwd_workspace_size(int(cu[-1]), w.heads) if w.varlen
+                  else bwd_workspace_size(w.batch, w.heads, w.seqlen))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step():
         if w.fp8:

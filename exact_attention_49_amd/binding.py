@@ -18,8 +18,8 @@ __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd
            "attn_fwd_splitkv",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "attn_bwd",
-           "attn_bwd_varlen", "attn_fwd_fp8", "attn_fwd_varlen_fp8", "library_path",
-           "load_library", "STATUS", "EXPORTED_SYMBOLS"]
+           "attn_bwd_varlen", "bwd_workspace_size", "varlen_bwd_workspace_size", "attn_fwd_fp8",
+           "attn_fwd_varlen_fp8", "library_path", "load_library", "STATUS", "EXPORTED_SYMBOLS"]
 
 LIB_NAME = "libexact_attn.so"
 
@@ -269,6 +269,16 @@ def attn_fwd_varlen_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def splitkv_num_splits(batch: int, heads: int, seqlen: int, head_dim: int) -> int:
     """The split count the library picks for num_splits = 0 (1 = no split)."""
     return load_library().attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim)
+
+
+def bwd_workspace_size(batch: int, heads_q: int, seqlen: int) -> int:
+    """Workspace bytes attn_bwd needs."""
+    return load_library().attn_bwd_workspace_size(batch, heads_q, seqlen)
+
+
+def varlen_bwd_workspace_size(total_tokens: int, heads_q: int) -> int:
+    """Workspace bytes attn_bwd_varlen needs."""
+    return load_library().attn_bwd_varlen_workspace_size(total_tokens, heads_q)
 
 
 def splitkv_workspace_size(batch: int, heads: int, seqlen: int, head_dim: int,

@@ -314,7 +314,8 @@ long varlen_slots(int rows, int num_seqs, int max_seqlen, int total_tokens) {
   return by_total < by_max ? by_total : by_max;
 }
 
-size_t bwd_workspace_bytes(long rows) { return rows > 0 ? align256((size_t)rows * 4) : 0; }
+// dPsum, then the LSE in log2 units: one fp32 per query row each, 256-byte aligned arrays.
+size_t bwd_workspace_bytes(long rows) { return rows > 0 ? 2 * align256((size_t)rows * 4) : 0; }
 
 // The gradient-side arguments of a backward call (the forward-side ones went through a Plan).
 int check_bwd_pointers(const float* lse, const void* dout, void* dq, void* dk, void* dv) {
@@ -346,6 +347,7 @@ int run_bwd(const Plan& p, int head_dim, int dtype, long q_slots, long k_slots, 
   b.dk = static_cast<uint16_t*>(dk);
   b.dv = static_cast<uint16_t*>(dv);
   b.dpsum = static_cast<float*>(workspace);
+  b.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)p.rows * 4));
   b.scale = scale;
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

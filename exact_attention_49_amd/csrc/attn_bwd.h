@@ -22,10 +22,12 @@
 //    blocks as the forward, with the roles of queries and keys exchanged: the mask is the
 //    forward's with the window bounds swapped (key j sees query i iff
 //    j - window_right <= i <= j + window_left).
-// Tiles are double-buffered in LDS: the dQ kernel loads K and V straight from global memory
-// into LDS (buffer_load ... lds), the dK/dV kernel stages Q, dO, LSE and dPsum through
-// registers.  An operand read both row-wise (MFMA A operand) and transposed
-// (ds_read_b64_tr_b16) is stored twice, once per swizzle.
+// Both kernels load their tiles straight from global memory into LDS (buffer_load ... lds).
+// An operand read both row-wise (MFMA A operand) and transposed (ds_read_b64_tr_b16) is
+// stored once, with the swizzle that serves both reads (swz_rt).  The dQ kernel double-buffers
+// K and V; the dK/dV kernel keeps three stages of Q, dO and the rows' LSE (log2 units, which
+// the dQ kernel writes beside dPsum) and dPsum, so that each tile's loads are in flight for a
+// step and a half.
 #pragma once
 
 #include "attn_common.h"
@@ -39,6 +41,7 @@ struct BwdArgs {
   uint16_t* dk;            // laid out as k
   uint16_t* dv;            // laid out as v
   float* dpsum;            // [rows of q]: written by the dQ kernel, read by the dK/dV kernel
+  float* lse2;             // [rows of q]: the LSE in log2 units, written and read likewise
   float scale;             // softmax scale (dQ and dK are multiplied by it)
   int ktiles_per_head;     // key-tile slots per key/value head (dK/dV kernel); the q-tile
                            // slots of the dQ kernel are f.tiles_per_head
@@ -122,7 +125,7 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
   const FwdArgs& a = ba.f;
   constexpr int BR = BwdShape::BR, BC = BwdShape::BC, NT = BwdShape::DQ_NT;
   constexpr int CH = D / 8, ROWB = D * 2, TILEB = BC * ROWB, LPT = BC * CH / NT;
-  constexpr int STAGEB = 3 * TILEB;  // K (row-read swizzle), K (transpose swizzle), V
+  constexpr int STAGEB = 2 * TILEB;  // K, V (shared swizzle: K is read both ways)
   static_assert(BC * CH % NT == 0, "tile must split evenly over the threads");
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGEB];
@@ -168,9 +171,12 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     for (int c = 0; c < D / 16; ++c) part += dot8<BF16>(dof[c], of[c]);
     dps = halves_sum(part);
   }
-  if (hh == 0 && qrow < seqlen) ba.dpsum[grow] = dps;
   const float lse2 = qrow < seqlen ? lse_to_log2(a.lse[grow]) : INFINITY;
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  if (hh == 0 && qrow < seqlen) {
+    ba.dpsum[grow] = dps;
+    ba.lse2[grow] = lse2;
+  }
+  const LaneOffsets<D> lo = lane_offsets<D, true>(lane);
   const float c2 = a.scale_log2;
 
   f32x16 dqacc[D / 32];
@@ -179,8 +185,8 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-  // K/V tiles go straight from global memory into LDS (buffer_load ... lds), K twice (one copy
-  // per read swizzle) and V once.  Instruction i of wave w fills the 16-byte LDS slots
+  // K/V tiles go straight from global memory into LDS (buffer_load ... lds), with the swizzle
+  // that serves both the row reads and K's transpose reads.  Instruction i of wave w fills the 16-byte LDS slots
   // (i * NW + w) * 64 + lane of a tile (row p / CH, chunk position p % CH): the lane fetches
   // the chunk that position holds.  One instruction round covers RROWS rows, a whole number of
   // swizzle periods, so instruction i reads instruction 0's bytes shifted by i rounds.
@@ -188,33 +194,28 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
   constexpr int RROWS = NW * 64 / CH;
   static_assert(RROWS % 16 == 0, "rounds must cover whole swizzle periods");
   const int drow = (wave * 64 + lane) / CH, dch = (wave * 64 + lane) % CH;
-  const int doff_n = drow * ROWB + ((dch ^ swz_k<D>(drow)) << 4);
-  const int doff_t = drow * ROWB + ((dch ^ swz_v<D>(drow)) << 4);
+  const int doff = drow * ROWB + ((dch ^ swz_rt<D>(drow)) << 4);
   const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * ROWB);
   const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * ROWB);
   const unsigned smem_a = lds_address(smem);
   auto dma_tile = [&](int t, int s) XATTN_INLINE {
     const int kbase = t * BC;
-    const unsigned knd = smem_a + s * STAGEB + wave * 1024, ktd = knd + TILEB, vnd = ktd + TILEB;
+    const unsigned kd = smem_a + s * STAGEB + wave * 1024, vd = kd + TILEB;
     if (kbase + BC <= seqlen) {
       static_for<LPT>([&](auto ic) XATTN_INLINE {
         constexpr int I = decltype(ic)::value;
         constexpr int L = I * NW * 1024, G = I * RROWS * ROWB;
-        buffer_load_lds16_at<L, G>(rsrc_k, doff_n, kbase * ROWB, knd);
-        buffer_load_lds16_at<L, G>(rsrc_k, doff_t, kbase * ROWB, ktd);
-        buffer_load_lds16_at<L, G>(rsrc_v, doff_n, kbase * ROWB, vnd);
+        buffer_load_lds16_at<L, G>(rsrc_k, doff, kbase * ROWB, kd);
+        buffer_load_lds16_at<L, G>(rsrc_v, doff, kbase * ROWB, vd);
       });
     } else {  // last tile: rows past the end re-read the sequence's last row (masked keys)
       static_for<LPT>([&](auto ic) XATTN_INLINE {
         constexpr int I = decltype(ic)::value;
         constexpr int L = I * NW * 1024;
         const int row = drow + I * RROWS;
-        const int crow = min(row, seqlen - 1 - kbase) * ROWB;
-        const int on = crow + ((dch ^ swz_k<D>(row)) << 4);
-        const int ot = crow + ((dch ^ swz_v<D>(row)) << 4);
-        buffer_load_lds16_at<L, 0>(rsrc_k, on, kbase * ROWB, knd);
-        buffer_load_lds16_at<L, 0>(rsrc_k, ot, kbase * ROWB, ktd);
-        buffer_load_lds16_at<L, 0>(rsrc_v, on, kbase * ROWB, vnd);
+        const int off = min(row, seqlen - 1 - kbase) * ROWB + ((dch ^ swz_rt<D>(row)) << 4);
+        buffer_load_lds16_at<L, 0>(rsrc_k, off, kbase * ROWB, kd);
+        buffer_load_lds16_at<L, 0>(rsrc_v, off, kbase * ROWB, vd);
       });
     }
   };
@@ -222,9 +223,8 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
   auto consume = [&](int t, int s) {
     const int k0 = t * BC;
     if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;
-    const char* kn = smem + s * STAGEB;
-    const char* kt = kn + TILEB;
-    const char* vn = kt + TILEB;
+    const char* kn = smem + s * STAGEB;  // read row-wise (S) and transposed (dQ)
+    const char* vn = kn + TILEB;
     f32x16 sacc[BC / 32], dpacc[BC / 32];
     __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
     mma_scores<BF16, D, BC>(kn, lo, qf, sacc);
@@ -243,7 +243,7 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     i32x4 dsf[BC / 16];
     pack_operand<BF16, BC>(sacc, dsf);
     __builtin_amdgcn_s_setprio(1);
-    mma_pv<BF16, D, BC>(kt, lo, dsf, dqacc);
+    mma_pv<BF16, D, BC, 3, true>(kn, lo, dsf, dqacc);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -317,15 +317,17 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   const FwdArgs& a = ba.f;
   constexpr int BK = BwdShape::BK, BQ = BwdShape::BQ, NT = BwdShape::NT;
   constexpr int CH = D / 8, ROWB = D * 2, TILEB = BQ * ROWB, LPT = BQ * CH / NT;
-  // per stage: Q (row-read swizzle), Q (transpose swizzle), dO (both), LSE2 and dPsum rows
-  constexpr int STAGEB = 4 * TILEB + 2 * BQ * 4;
+  // per stage: Q and dO (the shared swizzle: each is read both ways), then the rows' LSE (log2
+  // units) and dPsum; three stages, so that a tile's loads have a step and a half to arrive
+  constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;
+  constexpr int NSTAGE = 3;
   // P handed from each dV wave to its dK wave: per lane BQ / 2 fp32 scores as fp16
   constexpr int NPW = BQ / 16;  // 16-byte words per lane
   constexpr int PBUFB = (BwdShape::NW / 2) * NPW * 64 * 16;
   static_assert(BQ * CH % NT == 0 && BQ <= NT, "tile must split evenly over the threads");
   static_assert(BK == 32 * (BwdShape::NW / 2), "each key block has one dV and one dK wave");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGEB + PBUFB];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGEB + PBUFB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -338,7 +340,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   // staged rows stay in LDS until the second barrier of step t.
   const int pair = wave & (BwdShape::NW / 2 - 1);
   const bool dk_wave = wave >= BwdShape::NW / 2;
-  i32x4* pbuf = (i32x4*)(smem + 2 * STAGEB) + pair * NPW * 64 + lane;  // word c at [c * 64]
+  i32x4* pbuf = (i32x4*)(smem + NSTAGE * STAGEB) + pair * NPW * 64 + lane;  // word c at [c * 64]
 
   KeyWork w;
   if (!decode_key_work<BK>(ba, w)) return;
@@ -365,7 +367,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   // K (dV waves) or V (dK waves) rows of the lane's key
   i32x4 kvf[D / 16];
   load_q<D>((dk_wave ? a.v : a.k) + w.kv_row0 * D, krow, seqlen, hh, kvf);
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+  const LaneOffsets<D> lo = lane_offsets<D, true>(lane);
   const float c2 = a.scale_log2;
 
   f32x16 acc[D / 32];  // dV^T (dV waves) or dK^T / scale (dK waves)
@@ -374,56 +376,62 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  i32x4 stage_q[LPT], stage_d[LPT];
-  float stage_l = INFINITY, stage_p = 0.f;
   auto tile_base = [&](int it) {
     const int j = it / nq;
     return (qt_lo + it - j * nq) * BQ;
   };
-  auto gload = [&](int it) {
+  // Tile it (query head j of the group, rows qbase ..) straight from global memory into LDS
+  // stage st: Q and dO with 16-byte loads (instruction i of wave w fills the 16-byte slots
+  // (i * NW + w) * 64 + lane: row p / CH, chunk position p % CH, which holds chunk
+  // (p % CH) ^ swz_rt(row)), and one 4-byte load each for the rows' LSE (wave 0) and dPsum
+  // (wave 1).  Rows past the end of the sequence re-read its last row: their scores are masked.
+  constexpr int NW = BwdShape::NW;
+  constexpr int RROWS = NW * 64 / CH;  // rows per instruction round, whole swizzle periods
+  static_assert(RROWS % 16 == 0 && BQ == 64, "tile split");
+  const int drow = (wave * 64 + lane) / CH, dch = (wave * 64 + lane) % CH;
+  const int doff = drow * ROWB + ((dch ^ swz_rt<D>(drow)) << 4);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned smem_a = lds_address(smem);
+  auto dma_tile = [&](int it, int st) XATTN_INLINE {
     const int j = it / nq;
     const int qbase = (qt_lo + it - j * nq) * BQ;
     const long hrow = w.q_row0 + j * w.q_stride;  // row of token 0 of query head j
-    const uint16_t* qp = a.q + hrow * D;
-    const uint16_t* dp = ba.dout + hrow * D;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      const int q = qbase + r;
-      if (q < seqlen) {
-        stage_q[u] = ((const i32x4*)(qp + (long)q * D))[c];
-        stage_d[u] = ((const i32x4*)(dp + (long)q * D))[c];
-      } else {
-        stage_q[u] = (i32x4){0, 0, 0, 0};
-        stage_d[u] = (i32x4){0, 0, 0, 0};
-      }
+    const i32x4 rsrc_q = make_rsrc(a.q + hrow * D, (unsigned)seqlen * ROWB);
+    const i32x4 rsrc_d = make_rsrc(ba.dout + hrow * D, (unsigned)seqlen * ROWB);
+    const unsigned qd = smem_a + st * STAGEB + wave * 1024, dd = qd + TILEB;
+    if (qbase + BQ <= seqlen) {
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        constexpr int L = I * NW * 1024, G = I * RROWS * ROWB;
+        buffer_load_lds16_at<L, G>(rsrc_q, doff, qbase * ROWB, qd);
+        buffer_load_lds16_at<L, G>(rsrc_d, doff, qbase * ROWB, dd);
+      });
+    } else {
+      static_for<LPT>([&](auto ic) XATTN_INLINE {
+        constexpr int I = decltype(ic)::value;
+        constexpr int L = I * NW * 1024;
+        const int row = drow + I * RROWS;
+        const int off = min(row, seqlen - 1 - qbase) * ROWB + ((dch ^ swz_rt<D>(row)) << 4);
+        buffer_load_lds16_at<L, 0>(rsrc_q, off, qbase * ROWB, qd);
+        buffer_load_lds16_at<L, 0>(rsrc_d, off, qbase * ROWB, dd);
+      });
     }
-    if (tid < BQ) {
-      const int q = qbase + tid;
-      stage_l = q < seqlen ? lse_to_log2(a.lse[hrow + q]) : INFINITY;
-      stage_p = q < seqlen ? ba.dpsum[hrow + q] : 0.f;
+    if (wave_s < 2) {  // wave 0: the rows' LSE (log2 units), wave 1: their dPsum
+      const float* src = (wave_s == 0 ? ba.lse2 : ba.dpsum) + hrow;
+      const i32x4 rsrc_s = make_rsrc(src, (unsigned)seqlen * 4);
+      const int row = min(qbase + lane, seqlen - 1);
+      buffer_load_lds4(rsrc_s, row * 4, 0, smem_a + st * STAGEB + 2 * TILEB + wave_s * BQ * 4);
     }
   };
-  auto lstore = [&](int s) {
-    char* qn = smem + s * STAGEB;
-    char* qt = qn + TILEB;
-    char* dn = qt + TILEB;
-    char* dt = dn + TILEB;
-    float* ls = (float*)(dt + TILEB);
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int id = tid + u * NT;
-      const int r = id / CH, c = id % CH;
-      *(i32x4*)(qn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_q[u];
-      *(i32x4*)(qt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_q[u];
-      *(i32x4*)(dn + r * ROWB + ((c ^ swz_k<D>(r)) << 4)) = stage_d[u];
-      *(i32x4*)(dt + r * ROWB + ((c ^ swz_v<D>(r)) << 4)) = stage_d[u];
-    }
-    if (tid < BQ) {
-      ls[tid] = stage_l;
-      ls[BQ + tid] = stage_p;
-    }
+  // wait for the loads of all but the newest tile (when `newer`, the 2 LPT + 1 or 2 LPT load
+  // instructions of a later tile may stay outstanding)
+  auto wait_older = [&](bool newer) XATTN_INLINE {
+    if (!newer)
+      wait_vmem();
+    else if (wave_s < 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPT) : "memory");
   };
   // whether the pair's keys see any query of the tile at qbase
   auto tile_active = [&](int qbase) {
@@ -436,8 +444,8 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   i32x4 ph[NPW];
   auto consume_dv = [&](int qbase, int s) {
     const char* qn = smem + s * STAGEB;
-    const char* dt = qn + 3 * TILEB;
-    const float* ls = (const float*)(dt + TILEB);
+    const char* dn = qn + TILEB;
+    const float* ls = (const float*)(dn + TILEB);
     f32x16 sacc[BQ / 32];
     __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
     mma_scores<BF16, D, BQ>(qn, lo, kvf, sacc);
@@ -463,16 +471,15 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
 #pragma unroll
       for (int c = 0; c < NPW; ++c) ph[c] = pf[c];
     __builtin_amdgcn_s_setprio(1);
-    mma_pv<BF16, D, BQ>(dt, lo, pf, acc);
+    mma_pv<BF16, D, BQ, 3, true>(dn, lo, pf, acc);
     __builtin_amdgcn_s_setprio(0);
   };
 
   // dK wave, tile it (stage s, P of the tile in pbuf): dP = dO V^T, dS, dK^T += Q^T dS.
   auto consume_dk = [&](int s) {
     const char* qn = smem + s * STAGEB;
-    const char* qt = qn + TILEB;
-    const char* dn = qt + TILEB;
-    const float* ls = (const float*)(dn + 2 * TILEB);
+    const char* dn = qn + TILEB;
+    const float* ls = (const float*)(dn + TILEB);
     f32x16 dpacc[BQ / 32];
     __builtin_amdgcn_s_setprio(1);
     mma_scores<BF16, D, BQ>(dn, lo, kvf, dpacc);
@@ -500,30 +507,37 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
     i32x4 dsf[BQ / 16];
     pack_operand<BF16, BQ>(dpacc, dsf);
     __builtin_amdgcn_s_setprio(1);
-    mma_pv<BF16, D, BQ>(qt, lo, dsf, acc);
+    mma_pv<BF16, D, BQ, 3, true>(qn, lo, dsf, acc);
     __builtin_amdgcn_s_setprio(0);
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // Tile it lives in stage it % 3.  Step it: the dV waves consume tile it, the dK waves tile
+  // it - 1; after the first barrier stage (it + 2) % 3 = (it - 1) % 3 is free and receives tile
+  // it + 2; before the second, tile it + 1 (loaded during step it - 1) must have arrived.
+  dma_tile(0, 0);
+  if (n_it > 1) dma_tile(1, 1);
+  wait_older(n_it > 1);
+  block_barrier();
+  int s = 0;  // it % 3
   for (int it = 0; it < n_it; ++it) {
-    const int s = it & 1;
-    if (it + 1 < n_it) gload(it + 1);
+    const int sp = s == 0 ? 2 : s - 1;  // (it - 1) % 3 = (it + 2) % 3
     const bool act = tile_active(tile_base(it));
     if (!dk_wave) {
       if (act) consume_dv(tile_base(it), s);
     } else if (it >= 1 && tile_active(tile_base(it - 1))) {
-      consume_dk(s ^ 1);
+      consume_dk(sp);
     }
-    __syncthreads();  // the dK waves are done with stage s ^ 1 and with the P of tile it - 1
+    block_barrier();  // the dK waves are done with stage sp and with the P of tile it - 1
+    if (it + 2 < n_it) dma_tile(it + 2, sp);
     if (!dk_wave && act)
 #pragma unroll
       for (int c = 0; c < NPW; ++c) pbuf[c * 64] = ph[c];
-    if (it + 1 < n_it) lstore(s ^ 1);
-    __syncthreads();
+    if (it + 1 < n_it) wait_older(it + 2 < n_it);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the P words are in LDS
+    block_barrier();
+    s = s == 2 ? 0 : s + 1;
   }
-  if (dk_wave && tile_active(tile_base(n_it - 1))) consume_dk((n_it - 1) & 1);
+  if (dk_wave && tile_active(tile_base(n_it - 1))) consume_dk((n_it - 1) % 3);
 
   if (wave_active && krow < seqlen) {
     if (dk_wave)

@@ -183,6 +183,22 @@ __device__ __forceinline__ void buffer_load_lds16_at(i32x4 rsrc, int voff, int s
       : "memory", "scc");
 }
 
+// 4 bytes per lane from buffer `rsrc` at voff + soff straight into LDS at lds_base + 4 * lane
+// (buffer_load_dword ... lds); completion as for buffer_load_lds16.
+__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, int voff, int soff,
+                                                 unsigned lds_base) {
+  int saved;
+  const i32x4 rs = {__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rs),
+        "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(unsigned long long)((__attribute__((address_space(3))) const char*)p);
@@ -217,6 +233,14 @@ template <int D> __device__ __forceinline__ int swz_k(int r) {
 }
 template <int D> __device__ __forceinline__ int swz_v(int r) {
   return D >= 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+// One swizzle for a tile read both ways (32-row ds_read_b128 and 8-row ds_read_b64_tr_b16),
+// measured free of bank conflicts for both on gfx950: a bijection on 16 consecutive rows (two
+// rows per 256-byte bank line at d = 64) whose top two bits take each value twice over any 8
+// aligned rows, so every 64-byte quarter of the bank line is hit twice by a transpose read.
+template <int D> __device__ __forceinline__ int swz_rt(int r) {
+  static_assert(D == 64 || D == 128, "shared swizzle for head dims 64 and 128");
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -344,6 +368,8 @@ struct LaneOffsets {
   static constexpr int NV = D / 32 < 4 ? D / 32 : 4;  // distinct V offsets (column blocks mod 4)
   int k[NK];  // K read of d-chunk c: row l32, 16-byte chunk (2c + hh) swizzled
   int v[NV];  // first V transpose read of column block db (add 8 rows for the second)
+  int v8[NV];  // shared swizzle only: the second transpose read (8 rows further), whose rows
+               // have a different swizzle than the first's
   // byte offset (within a tile) of the K operand of d-chunk c and 32-key block kb
   __device__ __forceinline__ int kofs(int c, int kb) const {
     return k[c % NK] + (c / NK) * 256 + kb * 32 * D * 2;
@@ -352,21 +378,33 @@ struct LaneOffsets {
   __device__ __forceinline__ int vofs(int db, int kc) const {
     return v[db % NV] + (db / NV) * 256 + 16 * kc * D * 2;
   }
+  __device__ __forceinline__ int vofs8(int db, int kc) const {
+    return v8[db % NV] + (db / NV) * 256 + 16 * kc * D * 2;
+  }
 };
 
-template <int D>
+// RT: the tiles use the shared swizzle swz_rt for both read patterns.
+template <int D, bool RT = false>
 __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane) {
   constexpr int ROWB = D * 2;
   const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4, i16 = lane & 15;
+  auto sk = [](int r) {
+    if constexpr (RT) return swz_rt<D>(r); else return swz_k<D>(r);
+  };
+  auto sv = [](int r) {
+    if constexpr (RT) return swz_rt<D>(r); else return swz_v<D>(r);
+  };
   LaneOffsets<D> o;
 #pragma unroll
   for (int c = 0; c < LaneOffsets<D>::NK; ++c)
-    o.k[c] = l32 * ROWB + (((2 * c + hh) ^ swz_k<D>(l32)) << 4);
+    o.k[c] = l32 * ROWB + (((2 * c + hh) ^ sk(l32)) << 4);
   const int vrow = 4 * (g >> 1) + (i16 >> 2);
 #pragma unroll
   for (int db = 0; db < LaneOffsets<D>::NV; ++db) {
     const int col = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-    o.v[db] = vrow * ROWB + (((col >> 3) ^ swz_v<D>(vrow)) << 4) + ((col & 7) << 1);
+    o.v[db] = vrow * ROWB + (((col >> 3) ^ sv(vrow)) << 4) + ((col & 7) << 1);
+    if constexpr (RT)
+      o.v8[db] = (vrow + 8) * ROWB + (((col >> 3) ^ sv(vrow + 8)) << 4) + ((col & 7) << 1);
   }
   return o;
 }
@@ -517,15 +555,18 @@ __device__ __forceinline__ void scale_o(f32x16 (&o)[D / 32], float alpha) {
 // 16 kc + 8 + 4 hh + {0..3}: the key slots the S^T accumulator gave P.  Two transpose reads
 // fetch them.  Steps alternate the column blocks (independent accumulators); the operand of
 // step i + PF - 1 is read before the MFMA of step i; hook(i) runs at the start of step i.
-template <bool BF16, int D, int BC, int PF = 3, class Hook = NoHook>
+// RT: the tile uses the shared swizzle (lane_offsets<D, true>), whose second 8-row read has
+// its own offset.
+template <bool BF16, int D, int BC, int PF = 3, bool RT = false, class Hook = NoHook>
 __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
                                        const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32],
                                        const Hook& hook = Hook()) {
   constexpr int ROWB = D * 2, DB = D / 32, N = (BC / 16) * DB;
   auto read = [&](int i) XATTN_INLINE {
     const char* p = vt + lo.vofs(i % DB, i / DB);
+    const char* p8 = RT ? vt + lo.vofs8(i % DB, i / DB) : p + 8 * ROWB;
     const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
-    const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p + 8 * ROWB));
+    const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p8));
     return (i32x4){a[0], a[1], b[0], b[1]};
   };
   i32x4 buf[PF];

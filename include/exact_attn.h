@@ -208,9 +208,10 @@ int attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, void* o, fl
  *                   16-byte aligned DEVICE arrays owned by the caller; dq, dk, dv are fully
  *                   overwritten and must not alias any input.
  *   workspace     : DEVICE memory owned by the caller, 256-byte aligned, of at least
- *                   attn_bwd_workspace_size / attn_bwd_varlen_workspace_size bytes (one fp32
- *                   per query row: dPsum); otherwise ATTN_ERR_INVALID_ARG.  Its contents on
- *                   entry do not matter; two calls in flight at once must not share it.
+ *                   attn_bwd_workspace_size / attn_bwd_varlen_workspace_size bytes (two fp32
+ *                   per query row: dPsum and the LSE in log2 units, each array padded to 256
+ *                   bytes); otherwise ATTN_ERR_INVALID_ARG.  Its contents on entry do not
+ *                   matter; two calls in flight at once must not share it.
  *   head_dim      : 64 or 128 (ATTN_ERR_UNSUPPORTED_HEAD_DIM otherwise).
  * Two kernels run on `stream`, deterministically (no atomics).  Other errors as for the
  * forward.

@@ -283,10 +283,12 @@ def test_bwd_rejects_bad_arguments(lib, call, kw, status):
 
 
 def test_bwd_workspace_size(lib):
-    assert lib.attn_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 4
-    assert lib.attn_bwd_workspace_size(1, 3, 5) == 256          # 60 bytes, 256-byte granules
+    # two fp32 arrays of one value per query row (dPsum, LSE in log2 units), each padded to
+    # whole 256-byte granules
+    assert lib.attn_bwd_workspace_size(2, 32, 8192) == 2 * (2 * 32 * 8192 * 4)
+    assert lib.attn_bwd_workspace_size(1, 3, 5) == 2 * 256      # 60 bytes each
     assert lib.attn_bwd_workspace_size(0, 3, 5) == 0
-    assert lib.attn_bwd_varlen_workspace_size(1000, 6) == 24064
+    assert lib.attn_bwd_varlen_workspace_size(1000, 6) == 2 * 24064
     assert lib.attn_bwd_varlen_workspace_size(0, 6) == 0
 
 
