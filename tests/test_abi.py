@@ -292,6 +292,24 @@ def test_bwd_workspace_size(lib):
     assert lib.attn_bwd_varlen_workspace_size(0, 6) == 0
 
 
+def test_bwd_rejects_a_workspace_one_byte_short(lib):
+    # b = 1, heads_q = 2, n = 256: 512 query rows, two arrays of 2048 bytes
+    need = lib.attn_bwd_workspace_size(1, 2, 256)
+    assert need == 4096
+    assert call_bwd(lib, wsb=need - 1) == 1
+    need_v = lib.attn_bwd_varlen_workspace_size(16, 2)   # 32 rows: two 256-byte arrays
+    assert need_v == 512
+    assert call_bwd_varlen(lib, wsb=need_v - 1) == 1
+
+
+def test_binding_bwd_workspace_helpers_match_the_library(lib):
+    for args in [(2, 32, 8192), (1, 3, 5), (0, 3, 5), (3, 7, 1000)]:
+        assert binding.bwd_workspace_size(*args) == lib.attn_bwd_workspace_size(*args)
+    for args in [(1000, 6), (0, 6), (12345, 5)]:
+        assert (binding.varlen_bwd_workspace_size(*args)
+                == lib.attn_bwd_varlen_workspace_size(*args))
+
+
 def test_bwd_empty_problem_is_a_no_op(lib):
     assert call_bwd(lib, b=0, ws=None, wsb=0) == 0
     assert call_bwd_varlen(lib, ns=0, ws=None, wsb=0) == 0
