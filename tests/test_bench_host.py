@@ -29,3 +29,29 @@ def test_visible_pairs_closed_forms():
     # causal with a left window of w: row i sees min(i, w) + 1 keys
     w = 17
     assert bench.visible_pairs(n, True, w, 0) == sum(min(i, w) + 1 for i in range(n))
+
+
+def test_kernel_names_mirror_the_dispatch_thresholds():
+    """bench.py names the kernel the library launches: the ping-pong kernel at d = 128 once
+    the 256-row grid reaches 256 workgroups (384 under a causal or window mask)."""
+    from exact_attention_49_amd import inputs
+
+    def w(**kw):
+        base = dict(name="t", heads=8, head_dim=128, dtype="bf16", causal=False, seed=1,
+                    batch=1, seqlen=8192)
+        base.update(kw)
+        return inputs.Workload(**base)
+
+    assert bench.kernel_name(w()) == "attn_fwd_pp_kernel"                    # 256 tiles
+    assert bench.kernel_name(w(heads=4)) == "attn_fwd_kernel"                # 128 tiles
+    assert bench.kernel_name(w(causal=True)) == "attn_fwd_kernel"            # 256 masked
+    assert bench.kernel_name(w(causal=True, heads=12)) == "attn_fwd_pp_kernel"  # 384 masked
+    assert bench.kernel_name(w(window_left=1024)) == "attn_fwd_kernel"
+    assert bench.kernel_name(w(window_left=8192)) == "attn_fwd_pp_kernel"    # covers every key
+    assert bench.kernel_name(w(head_dim=64)) == "attn_fwd_kernel"
+    assert bench.kernel_name(w(head_dim=512)) == "attn_fwd_wide_kernel"
+    named = {n: bench.kernel_name(x) for n, x in inputs.WORKLOADS.items() if not x.varlen}
+    assert named["causal_bf16_d128_n8192"] == "attn_fwd_pp_kernel"
+    assert named["causal_bf16_d128_n2048"] == "attn_fwd_pp_kernel"
+    assert named["dense_fp16_d512_n4096"] == "attn_fwd_wide_kernel"
+    assert named["fp8_causal_d128_n8192"] == "attn_fwd_fp8_kernel"
