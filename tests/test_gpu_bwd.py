@@ -170,3 +170,14 @@ def test_bwd_binding_errors():
     q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(AttnError):
         attn_bwd(q, q, q, q, lse, q[:, :1].contiguous())   # dO shape
+
+
+def test_bwd_masked_grid_with_partial_last_group():
+    """B1 H13 N600 causal: the dQ kernel's 256-row q-tiles (3 per head) put its 13 (batch,
+    head) pairs in work-order groups of 2 with a last group of 1."""
+    _announce("bwd grouped order B1 H13 N600 causal")
+    m = MASKS["causal"]
+    q, k, v = inputs.make_dense(1, 13, 600, 64, "bf16", seed=3100)
+    do = inputs.make_upstream(q.shape, "bf16", seed=3101)
+    _check(_gpu_dense(q, k, v, do, m), _ref_dense(q, k, v, do, 64, m), torch.bfloat16,
+           "B1 H13 N600")

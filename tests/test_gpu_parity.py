@@ -243,3 +243,34 @@ def test_binding_errors_on_gpu_tensors():
     cu = torch.tensor([0, 8], dtype=torch.int32, device=dev)
     with pytest.raises(AttnError, match="INVALID_ARG"):
         attn_fwd_varlen(z, z, z, cu, max_seqlen=9)
+
+
+# Masked dense grids whose (batch, head) pairs split into work-order groups of G > 1 pairs
+# with a smaller last group (G = min(ceil(pairs / 8), ceil(32 / q-tiles per head))):
+#   B1 H13 N300 d64: 13 pairs, 3 tiles of 128 rows -> G = 2, groups 2,2,2,2,2,2,1
+#   B3 H3 N1000 d128 (generic kernel, 36 big tiles): 9 pairs, 8 tiles -> G = 2, last group 1
+@pytest.mark.parametrize("shape", [(1, 13, 300, 64), (3, 3, 1000, 128)])
+@pytest.mark.parametrize("mask", ["causal", "causal_w37"])
+def test_dense_masked_grid_with_partial_last_group(shape, mask):
+    b, h, n, d = shape
+    _announce(f"dense grouped order {shape} {mask}")
+    m = MASKS[mask]
+    q, k, v = inputs.make_dense(b, h, n, d, "bf16", seed=300 + h + d)
+    o, lse = gpu_dense(q, k, v, m["causal"], m["wl"], m["wr"])
+    o_ref, lse_ref = oracle_dense(q, k, v, 1 / math.sqrt(d), m["causal"], m["wl"], m["wr"])
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"{shape} {mask}")
+
+
+def test_pingpong_masked_grid_with_partial_last_group():
+    """B1 H50 N2048 d128 causal: 400 big tiles (ping-pong kernel), 8 tiles per head -> groups of
+    G = 4 pairs with a last group of 2.  Heads from the first, a middle and the last group are
+    compared with the oracle."""
+    _announce("ping-pong grouped order B1 H50 N2048 causal")
+    q, k, v = inputs.make_dense(1, 50, 2048, 128, "bf16", seed=350)
+    o, lse = gpu_dense(q, k, v, True)
+    for hd in (0, 3, 25, 47, 48, 49):
+        sl = slice(hd, hd + 1)
+        o_ref, lse_ref = oracle_dense(q[:, sl], k[:, sl], v[:, sl], 1 / math.sqrt(128), True,
+                                      -1, -1)
+        assert_close(to64(o[:, sl]), to64(lse[:, sl]), o_ref, lse_ref, torch.bfloat16,
+                     f"head {hd}")
