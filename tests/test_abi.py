@@ -179,6 +179,10 @@ def test_splitkv_automatic_count(lib):
     assert lib.attn_fwd_splitkv_num_splits(1, 1, 256, 128) == 1
     assert lib.attn_fwd_splitkv_num_splits(1, 1, 4096, 128) == 8
     assert lib.attn_fwd_varlen_splitkv_num_splits(2, 8192, 9000, 1, 64) >= 2
+    # enough work items for every CU's resident share: four small-shape workgroups per CU at
+    # d = 64 (2 heads x 128 q-tiles -> 4 splits), two at d = 128 (-> 2 splits)
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 64) == 4
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128) == 2
 
 
 @pytest.mark.parametrize("kw,status", [
