@@ -73,6 +73,8 @@ struct FwdArgs {
   long split_rows;            // rows of one split's partial arrays (= rows of o)
   float* o_part;              // [num_splits][split_rows][D]
   float* lse_part;            // [num_splits][split_rows], natural log
+  // dense causal ping-pong launches only: the grid covers pairs of q-tiles (m, tiles - 1 - m)
+  int fold;
 };
 
 // The running max is only moved when a tile's row max exceeds it by more than this (in log2
@@ -321,6 +323,30 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
     c_prev = c_next;
   }
   return false;
+}
+
+// Folded causal grid: workgroup -> (batch, head) and the q-tile pair (tiles - 1 - m, m), whose
+// two tiles together see tiles + 1 key tiles, so every workgroup of a head does the same work.
+// Same grouped order as decode_work, over pairs.  `light` is m, or -1 when the pair is the
+// middle tile of an odd count.
+template <int BR>
+__device__ __forceinline__ void decode_work_fold(const FwdArgs& a, Work& w, int& light) {
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.tiles_per_head, per2 = (per + 1) / 2;
+  const int nbh = gridDim.x / per2;
+  const int G = min((nbh + 7) / 8, max(a.kv_group, (32 + per2 - 1) / per2));
+  const int g = wid / (G * per2);
+  const int r = wid - g * G * per2;
+  const int gsize = min(G, nbh - g * G);
+  const int m = r / gsize;
+  const int bh = g * G + (r - m * gsize);
+  w.tile = per - 1 - m;
+  light = (per - 1 - m != m) ? m : -1;
+  w.split = 0;
+  w.seqlen = a.seqlen;
+  w.row0 = (long)bh * a.seqlen;
+  const int b = bh / a.heads_q, h = bh - b * a.heads_q;
+  w.kv_row0 = ((long)b * (a.heads_q / a.kv_group) + h / a.kv_group) * a.seqlen;
 }
 
 // Split-KV: restrict the key-tile range [t_lo, t_lo + n) of a q-tile to the share of split

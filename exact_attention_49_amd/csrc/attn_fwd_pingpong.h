@@ -26,6 +26,10 @@
 //   h = 2j   : A softmax(j)              | B  O += V_{j-1} P_{j-1}, S_j = K_j Q^T
 //   h = 2j+1 : A  O += V_j P_j, S_{j+1}  | B softmax(j), and B issues the loads of U_{j+1}
 //   B waits for its loads of U_j at the end of h = 2j; the barrier then publishes them.
+//
+// Dense causal grids may be folded (FwdArgs::fold): a workgroup then runs q-tile tiles - 1 - m
+// and then q-tile m of its head, one after the other, so that every workgroup of a head does
+// the same work and they all stream the head's K/V in step.
 #pragma once
 
 #include <type_traits>
@@ -59,196 +63,209 @@ void attn_fwd_pp_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const bool grp_a = wave < 4;
 
-  Work w;
-  if (!decode_work<BR, MODE>(a, w)) return;
-  const int seqlen = w.seqlen;
-  int wl, wr;
-  mode_windows<MODE>(a, wl, wr);
+  Work w0;
+  int light = -1;
+  if (MODE == MASK_CAUSAL && a.fold) {
+    decode_work_fold<BR>(a, w0, light);
+  } else if (!decode_work<BR, MODE>(a, w0)) {
+    return;
+  }
+  auto run_tile = [&](const Work& w) XATTN_INLINE {
+    const int seqlen = w.seqlen;
+    int wl, wr;
+    mode_windows<MODE>(a, wl, wr);
 
-  const int q0 = w.tile * BR;
-  const int qw0 = q0 + wave * 32;                      // first row of this wave
-  const int q_last = min(q0 + BR, seqlen) - 1;         // last valid row of the workgroup
-  int k_lo = 0, k_hi = seqlen - 1;                     // keys any valid row can see
-  if (wl >= 0) k_lo = max(0, q0 - wl);
-  if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
-  const int t_lo = k_lo / BC;
-  const int n = k_hi / BC - t_lo + 1;                  // K/V tiles to sweep (>= 1)
+    const int q0 = w.tile * BR;
+    const int qw0 = q0 + wave * 32;                      // first row of this wave
+    const int q_last = min(q0 + BR, seqlen) - 1;         // last valid row of the workgroup
+    int k_lo = 0, k_hi = seqlen - 1;                     // keys any valid row can see
+    if (wl >= 0) k_lo = max(0, q0 - wl);
+    if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
+    const int t_lo = k_lo / BC;
+    const int n = k_hi / BC - t_lo + 1;                  // K/V tiles to sweep (>= 1)
 
-  const bool wave_active = qw0 < seqlen;
-  const int qw_last = min(qw0 + 32, seqlen) - 1;
-  int kw_lo = 0, kw_hi = seqlen - 1;                   // keys this wave's rows can see
-  if (wl >= 0) kw_lo = max(0, qw0 - wl);
-  if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
+    const bool wave_active = qw0 < seqlen;
+    const int qw_last = min(qw0 + 32, seqlen) - 1;
+    int kw_lo = 0, kw_hi = seqlen - 1;                   // keys this wave's rows can see
+    if (wl >= 0) kw_lo = max(0, qw0 - wl);
+    if (wr >= 0) kw_hi = min(seqlen - 1, qw_last + wr);
 
-  const uint16_t* __restrict__ kp = a.k + w.kv_row0 * D;
-  const uint16_t* __restrict__ vp = a.v + w.kv_row0 * D;
-  const int qrow = qw0 + l32;
+    const uint16_t* __restrict__ kp = a.k + w.kv_row0 * D;
+    const uint16_t* __restrict__ vp = a.v + w.kv_row0 * D;
+    const int qrow = qw0 + l32;
 
-  i32x4 qf[D / 16];
-  load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
-  const LaneOffsets<D> lo = lane_offsets<D>(lane);
+    i32x4 qf[D / 16];
+    load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
+    const LaneOffsets<D> lo = lane_offsets<D>(lane);
 
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = a.scale_log2;
-  f32x16 sacc[BC / 32];  // S^T of the tile between its MFMA block and its softmax
-  i32x4 pf[BC / 16];     // P of the tile between its softmax and its MFMA block
+    f32x16 oacc[D / 32];
+  #pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c2 = a.scale_log2;
+    f32x16 sacc[BC / 32];  // S^T of the tile between its MFMA block and its softmax
+    i32x4 pf[BC / 16];     // P of the tile between its softmax and its MFMA block
 
-  // ---- direct global -> LDS tile loads (group B only) ------------------------------------
-  // Loader wave lw, instruction i fills LDS 16-byte slots (i * LOADERS + lw) * 64 + lane.  Slot
-  // p holds row p / CH, chunk (p % CH) ^ swizzle(row); since LOADERS * 64 / CH rows is a whole
-  // number of swizzle periods, instruction i reads the bytes of instruction 0 shifted by
-  // i * 4096, so one per-lane offset serves all of them (the shift goes to the scalar offset).
-  const int lw = __builtin_amdgcn_readfirstlane(wave & 3);  // loader index within group B
-  static_assert((LOADERS * 64 / CH) % 16 == 0, "loader rows must cover whole swizzle periods");
-  const int lrow = (lw * 64 + lane) / CH;  // row of this lane's slot in instruction 0
-  const int lch = (lw * 64 + lane) % CH;
-  const int voff_k = lrow * D * 2 + ((lch ^ swz_k<D>(lrow)) << 4);
-  const int voff_v = lrow * D * 2 + ((lch ^ swz_v<D>(lrow)) << 4);
-  const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * D * 2);
-  const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * D * 2);
-  constexpr int ISTEP = LOADERS * 64 * 16;  // bytes per load instruction (all loader waves)
-  // instruction II of the load of K (is_k) or V tile r into the LDS buffer at `dst`
-  auto load_one = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
-    constexpr bool is_k = decltype(k_tile)::value;
-    constexpr int II = decltype(ii)::value;
-    const int kbase = (t_lo + r) * BC;
-    const unsigned lds = dst + lw * 1024;
-    if (kbase + BC <= seqlen) {
+    // ---- direct global -> LDS tile loads (group B only) ------------------------------------
+    // Loader wave lw, instruction i fills LDS 16-byte slots (i * LOADERS + lw) * 64 + lane.  Slot
+    // p holds row p / CH, chunk (p % CH) ^ swizzle(row); since LOADERS * 64 / CH rows is a whole
+    // number of swizzle periods, instruction i reads the bytes of instruction 0 shifted by
+    // i * 4096, so one per-lane offset serves all of them (the shift goes to the scalar offset).
+    const int lw = __builtin_amdgcn_readfirstlane(wave & 3);  // loader index within group B
+    static_assert((LOADERS * 64 / CH) % 16 == 0, "loader rows must cover whole swizzle periods");
+    const int lrow = (lw * 64 + lane) / CH;  // row of this lane's slot in instruction 0
+    const int lch = (lw * 64 + lane) % CH;
+    const int voff_k = lrow * D * 2 + ((lch ^ swz_k<D>(lrow)) << 4);
+    const int voff_v = lrow * D * 2 + ((lch ^ swz_v<D>(lrow)) << 4);
+    const i32x4 rsrc_k = make_rsrc(kp, (unsigned)seqlen * D * 2);
+    const i32x4 rsrc_v = make_rsrc(vp, (unsigned)seqlen * D * 2);
+    constexpr int ISTEP = LOADERS * 64 * 16;  // bytes per load instruction (all loader waves)
+    // instruction II of the load of K (is_k) or V tile r into the LDS buffer at `dst`
+    auto load_one = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
+      constexpr bool is_k = decltype(k_tile)::value;
+      constexpr int II = decltype(ii)::value;
+      const int kbase = (t_lo + r) * BC;
+      const unsigned lds = dst + lw * 1024;
+      if (kbase + BC <= seqlen) {
+        buffer_load_lds16_at<II * ISTEP, II * ISTEP>(is_k ? rsrc_k : rsrc_v, is_k ? voff_k : voff_v,
+                                                     kbase * D * 2, lds);
+      } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
+        const int row = lrow + II * (LOADERS * 64 / CH);
+        const int crow = min(row, seqlen - 1 - kbase);
+        const int sw = is_k ? swz_k<D>(row) : swz_v<D>(row);
+        buffer_load_lds16_at<II * ISTEP, 0>(is_k ? rsrc_k : rsrc_v,
+                                            crow * D * 2 + ((lch ^ sw) << 4), kbase * D * 2, lds);
+      }
+    };
+    // instruction II of the load of a tile that lies wholly inside the sequence
+    auto load_full = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
+      constexpr bool is_k = decltype(k_tile)::value;
+      constexpr int II = decltype(ii)::value;
       buffer_load_lds16_at<II * ISTEP, II * ISTEP>(is_k ? rsrc_k : rsrc_v, is_k ? voff_k : voff_v,
-                                                   kbase * D * 2, lds);
-    } else {  // last tile: rows past the end re-read the sequence's last row (finite data)
-      const int row = lrow + II * (LOADERS * 64 / CH);
-      const int crow = min(row, seqlen - 1 - kbase);
-      const int sw = is_k ? swz_k<D>(row) : swz_v<D>(row);
-      buffer_load_lds16_at<II * ISTEP, 0>(is_k ? rsrc_k : rsrc_v,
-                                          crow * D * 2 + ((lch ^ sw) << 4), kbase * D * 2, lds);
-    }
-  };
-  // instruction II of the load of a tile that lies wholly inside the sequence
-  auto load_full = [&](auto k_tile, int r, unsigned dst, auto ii) XATTN_INLINE {
-    constexpr bool is_k = decltype(k_tile)::value;
-    constexpr int II = decltype(ii)::value;
-    buffer_load_lds16_at<II * ISTEP, II * ISTEP>(is_k ? rsrc_k : rsrc_v, is_k ? voff_k : voff_v,
-                                                 (t_lo + r) * BC * D * 2, dst + lw * 1024);
-  };
-  auto load_all = [&](auto k_tile, int r, unsigned dst) XATTN_INLINE {
-    static_for<LI>([&](auto ii) XATTN_INLINE { load_one(k_tile, r, dst, ii); });
-  };
-  const std::true_type K_TILE;
-  const std::false_type V_TILE;
-  const unsigned k_lds0a = lds_address(k_lds0), k_lds1a = lds_address(k_lds1);
-  const unsigned v_lds0a = lds_address(v_lds0), v_lds1a = lds_address(v_lds1);
+                                                   (t_lo + r) * BC * D * 2, dst + lw * 1024);
+    };
+    auto load_all = [&](auto k_tile, int r, unsigned dst) XATTN_INLINE {
+      static_for<LI>([&](auto ii) XATTN_INLINE { load_one(k_tile, r, dst, ii); });
+    };
+    const std::true_type K_TILE;
+    const std::false_type V_TILE;
+    const unsigned k_lds0a = lds_address(k_lds0), k_lds1a = lds_address(k_lds1);
+    const unsigned v_lds0a = lds_address(v_lds0), v_lds1a = lds_address(v_lds1);
 
-  // ---- the three per-tile steps of a wave (r = tile index relative to t_lo) ---------------
-  auto sees = [&](int r) XATTN_INLINE {
-    const int k0 = (t_lo + r) * BC;
-    return wave_active && k0 <= kw_hi && k0 + BC - 1 >= kw_lo;
-  };
-  auto step_scores = [&](int r, const char* kt) XATTN_INLINE {
-    if (sees(r)) mma_scores<BF16, D, BC, PF>(kt, lo, qf, sacc);
-  };
-  // softmax of tile r; group B also issues the loads of U_{r+1} = {V_{r+1}, K_{r+2}}, one
-  // instruction every SL exponentials (all at once when the tile is not visible to the wave)
-  constexpr int NLD = 2 * LI, SL = (BC / 2) / NLD;
-  // (the d = 128 sliding-window variant runs out of registers with the second softmax copy)
-  constexpr bool SPREAD_LOADS = !(MODE == MASK_WINDOW && D > 64);
-  static_assert((BC / 2) % NLD == 0, "loads must spread evenly over the softmax");
-  auto step_softmax = [&](int r, bool ld_v, bool ld_k, unsigned vdst, unsigned kdst) XATTN_INLINE {
-    // spread the loads only in the common case (both tiles wanted and whole); otherwise issue
-    // them up front
-    const bool spread = SPREAD_LOADS && ld_v && ld_k && (t_lo + r + 3) * BC <= seqlen;
-    if (!spread) {
-      if (ld_v) load_all(V_TILE, r + 1, vdst);
-      if (ld_k) load_all(K_TILE, r + 2, kdst);
-    }
-    if (!sees(r)) {
-      if (spread) {
-        load_all(V_TILE, r + 1, vdst);
-        load_all(K_TILE, r + 2, kdst);
+    // ---- the three per-tile steps of a wave (r = tile index relative to t_lo) ---------------
+    auto sees = [&](int r) XATTN_INLINE {
+      const int k0 = (t_lo + r) * BC;
+      return wave_active && k0 <= kw_hi && k0 + BC - 1 >= kw_lo;
+    };
+    auto step_scores = [&](int r, const char* kt) XATTN_INLINE {
+      if (sees(r)) mma_scores<BF16, D, BC, PF>(kt, lo, qf, sacc);
+    };
+    // softmax of tile r; group B also issues the loads of U_{r+1} = {V_{r+1}, K_{r+2}}, one
+    // instruction every SL exponentials (all at once when the tile is not visible to the wave)
+    constexpr int NLD = 2 * LI, SL = (BC / 2) / NLD;
+    // (the d = 128 sliding-window variant runs out of registers with the second softmax copy)
+    constexpr bool SPREAD_LOADS = !(MODE == MASK_WINDOW && D > 64);
+    static_assert((BC / 2) % NLD == 0, "loads must spread evenly over the softmax");
+    auto step_softmax = [&](int r, bool ld_v, bool ld_k, unsigned vdst, unsigned kdst) XATTN_INLINE {
+      // spread the loads only in the common case (both tiles wanted and whole); otherwise issue
+      // them up front
+      const bool spread = SPREAD_LOADS && ld_v && ld_k && (t_lo + r + 3) * BC <= seqlen;
+      if (!spread) {
+        if (ld_v) load_all(V_TILE, r + 1, vdst);
+        if (ld_k) load_all(K_TILE, r + 2, kdst);
       }
-      return;
-    }
-    const int k0 = (t_lo + r) * BC;
-    const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
-                           (wl >= 0 && k0 < qw0 + 31 - wl);
-    if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
-    bool moved;
-    float alpha;
-    if (spread) {  // one load instruction every SL exponentials: V first, then K
-      alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved, [&](int i) XATTN_INLINE {
-        at_step<NLD, SL>(i, [&](auto l) XATTN_INLINE {
-          constexpr int L = decltype(l)::value;
-          sched_fence();  // keep the loads where they are placed
-          if constexpr (L < LI)
-            load_full(V_TILE, r + 1, vdst, std::integral_constant<int, L>{});
-          else
-            load_full(K_TILE, r + 2, kdst, std::integral_constant<int, L - LI>{});
-          sched_fence();
+      if (!sees(r)) {
+        if (spread) {
+          load_all(V_TILE, r + 1, vdst);
+          load_all(K_TILE, r + 2, kdst);
+        }
+        return;
+      }
+      const int k0 = (t_lo + r) * BC;
+      const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
+                             (wl >= 0 && k0 < qw0 + 31 - wl);
+      if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+      bool moved;
+      float alpha;
+      if (spread) {  // one load instruction every SL exponentials: V first, then K
+        alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved, [&](int i) XATTN_INLINE {
+          at_step<NLD, SL>(i, [&](auto l) XATTN_INLINE {
+            constexpr int L = decltype(l)::value;
+            sched_fence();  // keep the loads where they are placed
+            if constexpr (L < LI)
+              load_full(V_TILE, r + 1, vdst, std::integral_constant<int, L>{});
+            else
+              load_full(K_TILE, r + 2, kdst, std::integral_constant<int, L - LI>{});
+            sched_fence();
+          });
         });
-      });
-    } else {
-      alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
-    }
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
-  };
-  auto step_pv = [&](int r, const char* vt) XATTN_INLINE {
-    if (sees(r)) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
-  };
-
-  // ---- prologue: K_0 (buffer 1), V_0 and K_1 (buffer 0) ---------------------------------
-  if (!grp_a) {
-    load_all(K_TILE, 0, k_lds1a);
-    load_all(V_TILE, 0, v_lds0a);
-    if (n > 1) load_all(K_TILE, 1, k_lds0a);
-    wait_vmem();
-  }
-  block_barrier();
-  if (grp_a) step_scores(0, k_lds1);
-
-  // ---- main loop: two half-phases per tile, buffer parity P = j & 1 known at compile time ----
-  auto iteration = [&](int j, auto parity) XATTN_INLINE {
-    constexpr int P = decltype(parity)::value;
-    char* const kP = P ? k_lds1 : k_lds0;  // holds K_{j+1}
-    char* const kQ = P ? k_lds0 : k_lds1;  // holds K_j, then receives K_{j+2}
-    char* const vP = P ? v_lds1 : v_lds0;  // holds V_j
-    char* const vQ = P ? v_lds0 : v_lds1;  // holds V_{j-1}, then receives V_{j+1}
-    const unsigned kQa = P ? k_lds0a : k_lds1a;
-    const unsigned vQa = P ? v_lds0a : v_lds1a;
-    // half-phase 2j
-    if (grp_a) {
-      if (j < n) step_softmax(j, false, false, 0, 0);
-    } else {
-      __builtin_amdgcn_s_setprio(2);  // MFMA block: win issue over the partner's softmax
-      if (j >= 1) step_pv(j - 1, vQ);
-      if (j < n) step_scores(j, kQ);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
-    block_barrier();
-    // half-phase 2j+1
-    if (grp_a) {
-      __builtin_amdgcn_s_setprio(2);
-      if (j < n) {
-        step_pv(j, vP);
-        if (j + 1 < n) step_scores(j + 1, kP);
+      } else {
+        alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
       }
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      if (j < n) step_softmax(j, j + 1 < n, j + 2 < n, vQa, kQa);
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
+    };
+    auto step_pv = [&](int r, const char* vt) XATTN_INLINE {
+      if (sees(r)) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
+    };
+
+    // ---- prologue: K_0 (buffer 1), V_0 and K_1 (buffer 0) ---------------------------------
+    if (!grp_a) {
+      load_all(K_TILE, 0, k_lds1a);
+      load_all(V_TILE, 0, v_lds0a);
+      if (n > 1) load_all(K_TILE, 1, k_lds0a);
+      wait_vmem();
     }
     block_barrier();
-  };
-  for (int j = 0; j <= n; j += 2) {
-    iteration(j, std::integral_constant<int, 0>{});
-    if (j + 1 <= n) iteration(j + 1, std::integral_constant<int, 1>{});
-  }
+    if (grp_a) step_scores(0, k_lds1);
 
-  if (wave_active) store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+    // ---- main loop: two half-phases per tile, buffer parity P = j & 1 known at compile time ----
+    auto iteration = [&](int j, auto parity) XATTN_INLINE {
+      constexpr int P = decltype(parity)::value;
+      char* const kP = P ? k_lds1 : k_lds0;  // holds K_{j+1}
+      char* const kQ = P ? k_lds0 : k_lds1;  // holds K_j, then receives K_{j+2}
+      char* const vP = P ? v_lds1 : v_lds0;  // holds V_j
+      char* const vQ = P ? v_lds0 : v_lds1;  // holds V_{j-1}, then receives V_{j+1}
+      const unsigned kQa = P ? k_lds0a : k_lds1a;
+      const unsigned vQa = P ? v_lds0a : v_lds1a;
+      // half-phase 2j
+      if (grp_a) {
+        if (j < n) step_softmax(j, false, false, 0, 0);
+      } else {
+        __builtin_amdgcn_s_setprio(2);  // MFMA block: win issue over the partner's softmax
+        if (j >= 1) step_pv(j - 1, vQ);
+        if (j < n) step_scores(j, kQ);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
+      block_barrier();
+      // half-phase 2j+1
+      if (grp_a) {
+        __builtin_amdgcn_s_setprio(2);
+        if (j < n) {
+          step_pv(j, vP);
+          if (j + 1 < n) step_scores(j + 1, kP);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        if (j < n) step_softmax(j, j + 1 < n, j + 2 < n, vQa, kQa);
+      }
+      block_barrier();
+    };
+    for (int j = 0; j <= n; j += 2) {
+      iteration(j, std::integral_constant<int, 0>{});
+      if (j + 1 <= n) iteration(j + 1, std::integral_constant<int, 1>{});
+    }
+
+    if (wave_active) store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  };
+  run_tile(w0);
+  if (light >= 0) {  // the pair's second tile: the LDS buffers are free after the last barrier
+    Work w1 = w0;
+    w1.tile = light;
+    run_tile(w1);
+  }
 }
 
 }  // namespace xattn

@@ -274,3 +274,19 @@ def test_pingpong_masked_grid_with_partial_last_group():
                                       -1, -1)
         assert_close(to64(o[:, sl]), to64(lse[:, sl]), o_ref, lse_ref, torch.bfloat16,
                      f"head {hd}")
+
+
+def test_pingpong_folded_causal_odd_tile_count():
+    """B1 H256 N2304 d128 causal: 9 q-tiles of 256 rows per head, run as folded pairs
+    (8, 0), (7, 1), (6, 2), (5, 3) and the middle tile 4 alone; 1280 pairs fill five rounds of
+    256 CUs.  Work-order groups of 7 heads end in a group of 4.  Heads from the first, a middle
+    and the last group are compared with the oracle in full."""
+    _announce("ping-pong folded causal B1 H256 N2304")
+    q, k, v = inputs.make_dense(1, 256, 2304, 128, "bf16", seed=360)
+    o, lse = gpu_dense(q, k, v, True)
+    for hd in (0, 6, 7, 130, 251, 252, 255):
+        sl = slice(hd, hd + 1)
+        o_ref, lse_ref = oracle_dense(q[:, sl], k[:, sl], v[:, sl], 1 / math.sqrt(128), True,
+                                      -1, -1)
+        assert_close(to64(o[:, sl]), to64(lse[:, sl]), o_ref, lse_ref, torch.bfloat16,
+                     f"head {hd}")
