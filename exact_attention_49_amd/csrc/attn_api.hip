@@ -188,6 +188,7 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   a.heads_q = heads;
   a.kv_group = heads / heads_kv;
   a.num_splits = 1;
+  a.max_seqlen = seqlen;
   p.n_work = (long)batch * heads * a.tiles_per_head;
   // Dense causal ping-pong grids run q-tiles m and tiles - 1 - m in one workgroup: every
   // workgroup of a head then does the same work, so a head's workgroups start and finish
@@ -267,6 +268,7 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
   a.heads_q = heads;
   a.kv_group = heads / heads_kv;
   a.num_splits = 1;
+  a.max_seqlen = max_seqlen;
   p.n_work = (long)heads * slots;
   p.max_len = max_seqlen;
   return p;

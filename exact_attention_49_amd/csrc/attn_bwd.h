@@ -135,7 +135,11 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   Work w;
-  if (!decode_work<BR, MODE>(a, w)) return;
+  if (const Decoded dc = decode_work<BR, MODE>(a, w); dc != Decoded::Run) {
+    if (dc == Decoded::Malformed)  // dQ rows of the sequence: NaN
+      fill_nan_rows(ba.dq, w.row0 + w.bad_lo, w.row0 + w.bad_hi, D / 8);
+    return;
+  }
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);
@@ -271,12 +275,14 @@ struct KeyWork {
   long kv_row0;   // row of the sequence's token 0 in the k/v row space
   long q_row0;    // the same in the q row space, for the group's first query head
   long q_stride;  // rows between consecutive query heads
+  int bad_lo, bad_hi;  // Decoded::Malformed only: the sequence rows to fill with NaN
 };
 
 // Map this workgroup to (key tile, key/value head, batch | sequence).  Key tiles run in
-// ascending order: under a causal mask the first ones are seen by the most queries.
+// ascending order: under a causal mask the first ones are seen by the most queries.  Packed
+// sequences longer than max_seqlen decode as Malformed (see Decoded).
 template <int BK>
-__device__ __forceinline__ bool decode_key_work(const BwdArgs& ba, KeyWork& w) {
+__device__ __forceinline__ Decoded decode_key_work(const BwdArgs& ba, KeyWork& w) {
   const FwdArgs& a = ba.f;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   const int per = ba.ktiles_per_head;
@@ -288,27 +294,20 @@ __device__ __forceinline__ bool decode_key_work(const BwdArgs& ba, KeyWork& w) {
     w.kv_row0 = (long)bh * a.seqlen;
     w.q_row0 = (long)bh * g * a.seqlen;  // query head (b, kvh * g) = row block b*Hq + kvh*g
     w.q_stride = a.seqlen;
-    return true;
+    return Decoded::Run;
   }
   const int h = wid / per;
   const int slot = wid - h * per;
-  int acc = 0;
-  int c_prev = min(max(a.cu_seqlens[0], 0), a.total_tokens);
-  for (int s = 0; s < a.num_seqs; ++s) {
-    const int c_next = min(max(a.cu_seqlens[s + 1], c_prev), a.total_tokens);
-    const int nt = (c_next - c_prev + BK - 1) / BK;
-    if (slot < acc + nt) {
-      w.tile = slot - acc;
-      w.seqlen = c_next - c_prev;
-      w.kv_row0 = (long)h * a.total_tokens + c_prev;
-      w.q_row0 = (long)h * g * a.total_tokens + c_prev;
-      w.q_stride = a.total_tokens;
-      return true;
-    }
-    acc += nt;
-    c_prev = c_next;
-  }
-  return false;
+  int c0, len, t, nt;
+  const Decoded d = find_seq_tile(a, slot, BK, c0, len, t, nt);
+  if (d == Decoded::Skip) return d;
+  w.tile = t;
+  w.seqlen = len;
+  w.kv_row0 = (long)h * a.total_tokens + c0;
+  w.q_row0 = (long)h * g * a.total_tokens + c0;
+  w.q_stride = a.total_tokens;
+  if (d == Decoded::Malformed) malformed_rows(t, nt, BK, len, w.bad_lo, w.bad_hi);
+  return d;
 }
 
 template <bool BF16, int D, int MODE>
@@ -343,7 +342,13 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   i32x4* pbuf = (i32x4*)(smem + NSTAGE * STAGEB) + pair * NPW * 64 + lane;  // word c at [c * 64]
 
   KeyWork w;
-  if (!decode_key_work<BK>(ba, w)) return;
+  if (const Decoded dc = decode_key_work<BK>(ba, w); dc != Decoded::Run) {
+    if (dc == Decoded::Malformed) {  // dK and dV rows of the sequence: NaN
+      fill_nan_rows(ba.dk, w.kv_row0 + w.bad_lo, w.kv_row0 + w.bad_hi, D / 8);
+      fill_nan_rows(ba.dv, w.kv_row0 + w.bad_lo, w.kv_row0 + w.bad_hi, D / 8);
+    }
+    return;
+  }
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);
@@ -555,13 +560,9 @@ hipError_t launch_bwd(const BwdArgs& a, bool bf16, int mode, int n_q, int n_k,
 
 template <bool BF16, int D, int MODE>
 hipError_t launch_bwd_mode(const BwdArgs& a, int n_q, int n_k, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<BF16, D, MODE>), dim3(n_q), dim3(BwdShape::DQ_NT), 0,
-                     s, a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(attn_bwd_dq_kernel<BF16, D, MODE>, n_q, BwdShape::DQ_NT, s, a);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<BF16, D, MODE>), dim3(n_k), dim3(BwdShape::NT), 0,
-                     s, a);
-  return hipGetLastError();
+  return launch_kernel(attn_bwd_dkdv_kernel<BF16, D, MODE>, n_k, BwdShape::NT, s, a);
 }
 
 #define XATTN_DEFINE_BWD_LAUNCHER(D)                                                         \

@@ -75,6 +75,8 @@ struct FwdArgs {
   float* lse_part;            // [num_splits][split_rows], natural log
   // dense causal ping-pong launches only: the grid covers pairs of q-tiles (m, tiles - 1 - m)
   int fold;
+  // packed batches: the caller's bound on every sequence length (the grid is sized from it)
+  int max_seqlen;
 };
 
 // The running max is only moved when a tile's row max exceeds it by more than this (in log2
@@ -82,6 +84,17 @@ struct FwdArgs {
 // below 2^8, harmless in fp32 and in the 16-bit P operand, and the result is unchanged: O and
 // l are both taken relative to the same reference m, and LSE = m + log2(l).
 constexpr float RESCALE_SLACK = 8.0f;
+
+// Host: launch a kernel that takes one argument block, and return this launch's own status.
+// hipLaunchKernel reports the launch itself; hipGetLastError after a triple-chevron launch
+// would also return (and clear) an earlier error left by the caller's own HIP calls.
+template <class A>
+inline hipError_t launch_kernel(void (*kernel)(A), unsigned grid, unsigned block, hipStream_t s,
+                                const A& arg) {
+  void* args[] = {const_cast<A*>(&arg)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), args,
+                         0, s);
+}
 
 // ---------------------------------------------------------------------------------------------
 // Instruction wrappers
@@ -255,15 +268,83 @@ struct Work {
   long row0;   // index of the sequence's token 0 in the [*, D] row space of q/o and lse
   long kv_row0;  // the same for k/v (differs from row0 with grouped K/V heads)
   int split;   // split-KV: which share of the q-tile's key tiles (0 otherwise)
+  int bad_lo, bad_hi;  // Decoded::Malformed only: the sequence rows to fill with NaN
 };
+
+// What a workgroup's slot decodes to: nothing (a slot past the last tile), a tile to compute,
+// or a tile of a packed sequence longer than the caller's max_seqlen.  Such a sequence is never
+// computed or read (the grid and the kernels' 32-bit offsets are sized from max_seqlen): its
+// tiles are counted as if it had max_seqlen rows, so the grid still covers them, and their
+// workgroups fill every output row of the sequence with NaN instead, the last counted tile
+// taking the rows past max_seqlen as well.
+enum class Decoded { Skip, Run, Malformed };
+
+// Rows of a malformed sequence of `len` rows that counted tile t of nt (tiles of `rows`)
+// fills with NaN.
+__device__ __forceinline__ void malformed_rows(int t, int nt, int rows, int len, int& lo,
+                                               int& hi) {
+  lo = t * rows;
+  hi = (t == nt - 1) ? len : min(len, (t + 1) * rows);
+}
+
+// Walk the sequences of a packed batch to the one holding q-tile slot `slot` (tiles of
+// `rows` rows).  Sets the sequence's first token c0, its length len, the tile index t and the
+// sequence's tile count nt (counted with at most max_seqlen rows).  Returns Skip for a slot
+// past the last tile, Malformed for a sequence longer than max_seqlen.  Entries of cu_seqlens
+// are clamped so that malformed prefix sums cannot address outside [0, total_tokens).
+__device__ __forceinline__ Decoded find_seq_tile(const FwdArgs& a, int slot, int rows, int& c0,
+                                                 int& len, int& t, int& nt) {
+  int acc = 0;
+  int c_prev = min(max(a.cu_seqlens[0], 0), a.total_tokens);
+  for (int s = 0; s < a.num_seqs; ++s) {
+    const int c_next = min(max(a.cu_seqlens[s + 1], c_prev), a.total_tokens);
+    const int l = c_next - c_prev;
+    const int n = (min(l, a.max_seqlen) + rows - 1) / rows;
+    if (slot < acc + n) {
+      c0 = c_prev;
+      len = l;
+      t = slot - acc;
+      nt = n;
+      return l > a.max_seqlen ? Decoded::Malformed : Decoded::Run;
+    }
+    acc += n;
+    c_prev = c_next;
+  }
+  return Decoded::Skip;
+}
+
+// Fill rows [r0, r1) of a row-major array of `words` 16-byte words per row with all-ones bits
+// (a NaN in fp32, fp16 and bf16), with every thread of the workgroup.
+__device__ __forceinline__ void fill_nan_rows(void* base, long r0, long r1, int words) {
+  i32x4* p = (i32x4*)base + r0 * words;
+  const long n = (r1 - r0) * words;
+  for (long i = threadIdx.x; i < n; i += blockDim.x) p[i] = (i32x4){-1, -1, -1, -1};
+}
+__device__ __forceinline__ void fill_nan_f32(float* base, long r0, long r1) {
+  for (long i = r0 + threadIdx.x; i < r1; i += blockDim.x) base[i] = __uint_as_float(~0u);
+}
+
+// The forward's outputs for a malformed sequence's tile: O (or the split's fp32 partial O)
+// and LSE rows set to NaN.
+template <int D, bool SPLIT = false>
+__device__ __forceinline__ void fill_malformed_fwd(const FwdArgs& a, const Work& w) {
+  if constexpr (SPLIT) {
+    const long r = (long)w.split * a.split_rows + w.row0;
+    fill_nan_rows(a.o_part, r + w.bad_lo, r + w.bad_hi, D / 4);
+    fill_nan_f32(a.lse_part, r + w.bad_lo, r + w.bad_hi);
+  } else {
+    fill_nan_rows(a.o, w.row0 + w.bad_lo, w.row0 + w.bad_hi, D / 8);
+    if (a.lse != nullptr) fill_nan_f32(a.lse, w.row0 + w.bad_lo, w.row0 + w.bad_hi);
+  }
+}
 
 // Map this workgroup to (q-tile, head, batch | sequence) and, in split-KV mode, a split.
 // Dense batches: heads of all batch entries in order with the q-tiles of a head consecutive;
 // masked modes, whose later q-tiles see more keys, instead run each group of heads tile-major,
 // heaviest first.  Packed batches: the q-tile slots of a head walk the sequences in order;
-// slots past the last tile are unused.  Returns false for an unused slot.
+// slots past the last tile are unused (Skip).
 template <int BR, int MODE, bool SPLIT = false>
-__device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
+__device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
   int wid = xcd_remap(blockIdx.x, gridDim.x);
   w.split = 0;
   if constexpr (SPLIT) {  // the splits of one q-tile are neighbours (they share its Q rows)
@@ -301,28 +382,19 @@ __device__ __forceinline__ bool decode_work(const FwdArgs& a, Work& w) {
     // they run on the same XCD and share its L2 copy of the K/V head
     const int b = bh / a.heads_q, h = bh - b * a.heads_q;
     w.kv_row0 = ((long)b * (a.heads_q / a.kv_group) + h / a.kv_group) * a.seqlen;
-    return true;
+    return Decoded::Run;
   }
   const int h = wid / per;
   const int slot = wid - h * per;
-  int acc = 0;
-  int c_prev = min(max(a.cu_seqlens[0], 0), a.total_tokens);
-  for (int s = 0; s < a.num_seqs; ++s) {
-    // clamped so that malformed prefix sums cannot address outside [0, total_tokens)
-    const int c_next = min(max(a.cu_seqlens[s + 1], c_prev), a.total_tokens);
-    const int nt = (c_next - c_prev + BR - 1) / BR;
-    if (slot < acc + nt) {
-      const int t = slot - acc;
-      w.tile = (MODE != MASK_NONE) ? nt - 1 - t : t;
-      w.seqlen = c_next - c_prev;
-      w.row0 = (long)h * a.total_tokens + c_prev;
-      w.kv_row0 = (long)(h / a.kv_group) * a.total_tokens + c_prev;
-      return true;
-    }
-    acc += nt;
-    c_prev = c_next;
-  }
-  return false;
+  int c0, len, t, nt;
+  const Decoded d = find_seq_tile(a, slot, BR, c0, len, t, nt);
+  if (d == Decoded::Skip) return d;
+  w.tile = (MODE != MASK_NONE) ? nt - 1 - t : t;
+  w.seqlen = len;
+  w.row0 = (long)h * a.total_tokens + c0;
+  w.kv_row0 = (long)(h / a.kv_group) * a.total_tokens + c0;
+  if (d == Decoded::Malformed) malformed_rows(t, nt, BR, len, w.bad_lo, w.bad_hi);
+  return d;
 }
 
 // Folded causal grid: workgroup -> (batch, head) and the q-tile pair (tiles - 1 - m, m), whose

@@ -65,37 +65,33 @@ inline long big_tile_min_work(int mode) {
 
 template <bool BF16, int D, int MODE, class S, bool SPLIT> struct Launch;
 template <bool BF16, int D, int MODE> struct Launch<BF16, D, MODE, UsePingPong, false> {
-  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<BF16, D, MODE>), dim3(n_work),
-                       dim3(PingPongShape::NT), 0, s, a);
+  static hipError_t go(const FwdArgs& a, int n_work, hipStream_t s) {
+    return launch_kernel(attn_fwd_pp_kernel<BF16, D, MODE>, n_work, PingPongShape::NT, s, a);
   }
 };
 template <bool BF16, int D, int MODE, bool SPLIT> struct Launch<BF16, D, MODE, UseWide, SPLIT> {
-  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_wide_kernel<BF16, D, MODE, SPLIT>), dim3(n_work),
-                       dim3(WideShape::NT), 0, s, a);
+  static hipError_t go(const FwdArgs& a, int n_work, hipStream_t s) {
+    return launch_kernel(attn_fwd_wide_kernel<BF16, D, MODE, SPLIT>, n_work, WideShape::NT, s,
+                         a);
   }
 };
 template <bool BF16, int D, int MODE, class T, bool SPLIT>
 struct Launch<BF16, D, MODE, UseGeneric<T>, SPLIT> {
-  static void go(const FwdArgs& a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL((attn_fwd_kernel<BF16, D, MODE, T, SPLIT>), dim3(n_work), dim3(T::NT),
-                       0, s, a);
+  static hipError_t go(const FwdArgs& a, int n_work, hipStream_t s) {
+    return launch_kernel(attn_fwd_kernel<BF16, D, MODE, T, SPLIT>, n_work, T::NT, s, a);
   }
 };
 
 template <int D, class S, bool SPLIT = false>
 hipError_t launch_shape(const FwdArgs& a, bool bf16, int mode, int n_work, hipStream_t s) {
   if (bf16) {
-    if (mode == MASK_NONE) Launch<true, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
-    else if (mode == MASK_CAUSAL) Launch<true, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
-    else Launch<true, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
-  } else {
-    if (mode == MASK_NONE) Launch<false, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
-    else if (mode == MASK_CAUSAL) Launch<false, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
-    else Launch<false, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
+    if (mode == MASK_NONE) return Launch<true, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
+    if (mode == MASK_CAUSAL) return Launch<true, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
+    return Launch<true, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
   }
-  return hipGetLastError();
+  if (mode == MASK_NONE) return Launch<false, D, MASK_NONE, S, SPLIT>::go(a, n_work, s);
+  if (mode == MASK_CAUSAL) return Launch<false, D, MASK_CAUSAL, S, SPLIT>::go(a, n_work, s);
+  return Launch<false, D, MASK_WINDOW, S, SPLIT>::go(a, n_work, s);
 }
 
 // Split-KV runs on the small shape of a head dim (the one for grids too small to fill the
@@ -103,11 +99,8 @@ hipError_t launch_shape(const FwdArgs& a, bool bf16, int mode, int n_work, hipSt
 template <int D>
 hipError_t launch_merge_shape(const MergeArgs& m, bool bf16, hipStream_t s) {
   const long blocks = (m.rows + 3) / 4;
-  if (bf16)
-    hipLaunchKernelGGL((attn_merge_kernel<true, D>), dim3((unsigned)blocks), dim3(256), 0, s, m);
-  else
-    hipLaunchKernelGGL((attn_merge_kernel<false, D>), dim3((unsigned)blocks), dim3(256), 0, s, m);
-  return hipGetLastError();
+  if (bf16) return launch_kernel(attn_merge_kernel<true, D>, (unsigned)blocks, 256, s, m);
+  return launch_kernel(attn_merge_kernel<false, D>, (unsigned)blocks, 256, s, m);
 }
 
 // Host launchers for one head dim (explicitly specialised per head dim in its own translation

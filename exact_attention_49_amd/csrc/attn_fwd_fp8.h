@@ -110,7 +110,10 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   Work w;
-  if (!decode_work<BR, MODE>(a, w)) return;
+  if (const Decoded dc = decode_work<BR, MODE>(a, w); dc != Decoded::Run) {
+    if (dc == Decoded::Malformed) fill_malformed_fwd<D>(a, w);
+    return;
+  }
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);

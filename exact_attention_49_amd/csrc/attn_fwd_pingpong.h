@@ -67,7 +67,8 @@ void attn_fwd_pp_kernel(FwdArgs a) {
   int light = -1;
   if (MODE == MASK_CAUSAL && a.fold) {
     decode_work_fold<BR>(a, w0, light);
-  } else if (!decode_work<BR, MODE>(a, w0)) {
+  } else if (const Decoded dc = decode_work<BR, MODE>(a, w0); dc != Decoded::Run) {
+    if (dc == Decoded::Malformed) fill_malformed_fwd<D>(a, w0);
     return;
   }
   auto run_tile = [&](const Work& w) XATTN_INLINE {

@@ -153,7 +153,10 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   Work w;
-  if (!decode_work<BR, MODE, SPLIT>(a, w)) return;
+  if (const Decoded dc = decode_work<BR, MODE, SPLIT>(a, w); dc != Decoded::Run) {
+    if (dc == Decoded::Malformed) fill_malformed_fwd<D, SPLIT>(a, w);
+    return;
+  }
   const int seqlen = w.seqlen;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);

@@ -3,9 +3,10 @@
 // row's result is the combination that the online softmax would have produced over all keys:
 //     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
 // with splits that saw no key (LSE_s = -inf) contributing nothing, and O = 0, LSE = -inf when
-// no split saw a key.  This is the merge of partial softmax results that split-KV kernels use
-// (page "flash_fwd_kernel.h" @c272619: split-KV work items, n_split_idx); the formula is the
-// log-sum-exp identity written out.  One wave per row; each lane owns PER >= 2 columns.
+// no split saw a key.  A NaN partial (the rows of a packed sequence longer than max_seqlen)
+// makes the row's O and LSE NaN.  This is the merge of partial softmax results that split-KV
+// kernels use (page "flash_fwd_kernel.h" @c272619: split-KV work items, n_split_idx); the
+// formula is the log-sum-exp identity written out.  One wave per row; each lane owns PER >= 2 columns.
 #pragma once
 
 #include "attn_common.h"
@@ -28,8 +29,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
   const bool owns = lane * PER < D;
-  float m = -INFINITY;
-  for (int s = 0; s < a.num_splits; ++s) m = fmaxf(m, a.lse_part[(long)s * a.rows + row]);
+  float m = -INFINITY;  // the largest LSE_s, or NaN if any is NaN (fmaxf would drop a NaN)
+  for (int s = 0; s < a.num_splits; ++s) {
+    const float x = a.lse_part[(long)s * a.rows + row];
+    m = (x > m || x != x) ? x : m;
+  }
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   }
   if (a.lse != nullptr && lane == 0) {
     constexpr float LN2 = 0.693147180559945309f;
-    a.lse[row] = total > 0.f ? m + fast_log2(total) * LN2 : -INFINITY;
+    a.lse[row] = !(total <= 0.f) ? m + fast_log2(total) * LN2 : -INFINITY;  // NaN stays NaN
   }
 }
 

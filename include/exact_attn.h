@@ -27,8 +27,11 @@
  *     calling thread's last HIP error code, so concurrent calls from several threads are
  *     safe.
  *   - Errors are returned, never thrown or printed; nothing is launched when the arguments
- *     fail validation.  Arguments are validated on the host only: the contents of device
- *     arrays (cu_seqlens) are trusted.
+ *     fail validation.  Arguments are validated on the host; of the device arrays, cu_seqlens
+ *     entries are clamped into [0, total_tokens] and a sequence longer than max_seqlen gets
+ *     NaN rows (see attn_fwd_varlen).
+ *   - ATTN_ERR_HIP is the status of the kernel launch itself (hipLaunchKernel); an error left
+ *     on the thread by the caller's earlier HIP calls is neither returned nor cleared.
  *   - Supported head_dim: 64, 128, 256, 512.  Supported dtype: ATTN_DTYPE_FP16,
  *     ATTN_DTYPE_BF16.  Any sequence length is accepted (no tile-multiple requirement) up to
  *     seqlen * head_dim * 2 < 2^31 bytes per (sequence, head) (ATTN_ERR_TOO_LARGE beyond).
@@ -85,7 +88,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                are allowed.
  *   max_seqlen : host upper bound on every sequence length (>= 1 when total_tokens > 0); it
  *                only sizes the launch, so no device-to-host copy is needed.  A sequence
- *                longer than max_seqlen is not computed correctly.
+ *                longer than max_seqlen is an error the host cannot see: it is not computed
+ *                and none of its K/V rows are read; instead every row of it in o and lse
+ *                (every call that takes max_seqlen: dq/dk/dv in the backward, the partial
+ *                and merged rows in split-KV) is filled with NaN, and the other sequences are
+ *                computed as usual.
  * num_seqs, total_tokens >= 0 (zero is a no-op).  Masks apply per sequence, as above.
  */
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

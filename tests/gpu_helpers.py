@@ -75,3 +75,59 @@ def softmax_scale(d: int) -> float:
 def oracle_dense(q, k, v, scale, causal, wl, wr):
     return oracle.attention_dense(q.float().numpy(), k.float().numpy(), v.float().numpy(),
                                   scale, causal, wl, wr)
+
+
+def _oracle_workers() -> int:
+    # the oracle's elementwise passes run on one core; BLAS threads share the rest
+    import os
+    return max(1, min(8, (os.cpu_count() or 2) // 2))
+
+
+def check_all_heads_dense(q, k, v, o, lse, scale, causal, wl, wr, dtype, what=""):
+    """Every row of every (batch, head) of a dense result against the oracle, one head per
+    oracle call (query head h reads K/V head h // (H / Hkv)); heads run in a thread pool.
+    q, k, v are the CPU inputs, o and lse the GPU outputs (any device).  Returns the largest
+    O error."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    o, lse = o.cpu(), lse.cpu() if lse is not None else None
+    bsz, nh = q.shape[0], q.shape[1]
+    g = nh // k.shape[1]
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+
+    def one(bh):
+        b, h = bh
+        o_ref, lse_ref = oracle.attention_head(qf[b, h], kf[b, h // g], vf[b, h // g], scale,
+                                               causal, wl, wr)
+        return assert_close(to64(o[b, h]), None if lse is None else to64(lse[b, h]), o_ref,
+                            lse_ref, dtype, f"{what} b={b} h={h}")
+
+    pairs = [(b, h) for b in range(bsz) for h in range(nh)]
+    with ThreadPoolExecutor(_oracle_workers()) as ex:
+        errs = list(ex.map(one, pairs))
+    return max(errs)
+
+
+def check_all_heads_varlen(q, k, v, cu, o, lse, scale, causal, wl, wr, dtype, what=""):
+    """Every row of every (sequence, head) of a packed result against the oracle, one
+    (sequence, head) per oracle call, in a thread pool.  Returns the largest O error."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    o, lse = o.cpu(), lse.cpu() if lse is not None else None
+    nh = q.shape[0]
+    g = nh // k.shape[0]
+    qf, kf, vf = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    cu_l = [int(x) for x in cu.tolist()]
+
+    def one(sh):
+        s, h = sh
+        a, b = cu_l[s], cu_l[s + 1]
+        o_ref, lse_ref = oracle.attention_head(qf[h, a:b], kf[h // g, a:b], vf[h // g, a:b],
+                                               scale, causal, wl, wr)
+        return assert_close(to64(o[h, a:b]), None if lse is None else to64(lse[h, a:b]), o_ref,
+                            lse_ref, dtype, f"{what} seq={s} h={h}")
+
+    jobs = [(s, h) for s in range(len(cu_l) - 1) if cu_l[s + 1] > cu_l[s] for h in range(nh)]
+    with ThreadPoolExecutor(_oracle_workers()) as ex:
+        errs = list(ex.map(one, jobs))
+    return max(errs) if errs else 0.0

@@ -1,9 +1,8 @@
 """GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
 
 Small shapes are compared in full (they span several q-tiles and K/V tiles plus a ragged
-tail); the five named workloads are compared in full where the oracle is quick and on
-sampled rows (tile boundaries, both ends, random rows) where it is not, plus properties that
-hold at any size."""
+tail); the five named workloads are compared in full, every row of every head, in the launch
+configuration the benchmark times; plus properties that hold at any size."""
 
 import math
 
@@ -13,8 +12,8 @@ import torch
 
 import oracle
 from exact_attention_49_amd import AttnError, attn_fwd, attn_fwd_varlen, inputs
-from tests.gpu_helpers import (O_TOL, assert_close, gpu_dense, gpu_varlen, oracle_dense,
-                               sample_rows, to64)
+from tests.gpu_helpers import (O_TOL, assert_close, check_all_heads_dense,
+                               check_all_heads_varlen, gpu_dense, gpu_varlen, oracle_dense, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,79 +101,48 @@ def test_workload_tiny_fp16_d64_full():
     assert_close(to64(o), to64(lse), o_ref, lse_ref, w.torch_dtype, w.name)
 
 
-def _check_sampled_dense(w, q, k, v, o, lse, heads, rng):
-    idx = []
-    for (b, h) in heads:
-        idx += [(b, h, r) for r in sample_rows(w.seqlen, rng)]
-    idx = np.array(idx)
-    o_ref, lse_ref = oracle.attention_rows_dense(q.float(), k.float(), v.float(), idx,
-                                                 w.softmax_scale, w.causal, w.window_left,
-                                                 w.window_right)
-    og = o[idx[:, 0], idx[:, 1], idx[:, 2]]
-    lg = lse[idx[:, 0], idx[:, 1], idx[:, 2]]
-    return assert_close(to64(og), to64(lg), o_ref, lse_ref, w.torch_dtype, w.name)
-
-
 def _check_finite(o, lse):
     assert bool(torch.isfinite(o).all()), "non-finite O"
     assert bool(torch.isfinite(lse).all()), "non-finite LSE"
 
 
-def test_workload_causal_bf16_d128_n2048():
+def test_workload_causal_bf16_d128_n2048_full():
     w, q, k, v = _dense_workload("causal_bf16_d128_n2048")
     _announce(w.name)
     o, lse = gpu_dense(q, k, v, w.causal)
-    o, lse = o.cpu(), lse.cpu()
     _check_finite(o, lse)
-    # two whole heads in full, then sampled rows of other heads
-    for (b, h) in [(0, 0), (3, 15)]:
-        o_ref, lse_ref = oracle.attention_head(q[b, h].float().numpy(), k[b, h].float().numpy(),
-                                               v[b, h].float().numpy(), w.softmax_scale, True)
-        assert_close(to64(o[b, h]), to64(lse[b, h]), o_ref, lse_ref, w.torch_dtype, w.name)
-    rng = np.random.default_rng(7)
-    _check_sampled_dense(w, q, k, v, o, lse, [(1, 3), (2, 9), (3, 0)], rng)
+    check_all_heads_dense(q, k, v, o, lse, w.softmax_scale, w.causal, w.window_left,
+                          w.window_right, w.torch_dtype, w.name)
 
 
-def test_workload_causal_bf16_d128_n8192_sampled():
+def test_workload_causal_bf16_d128_n8192_full():
+    """Every row of all 64 (batch, head) pairs (the benchmark's launch: folded ping-pong
+    grid)."""
     w, q, k, v = _dense_workload("causal_bf16_d128_n8192")
     _announce(w.name)
     o, lse = gpu_dense(q, k, v, w.causal)
-    o, lse = o.cpu(), lse.cpu()
     _check_finite(o, lse)
-    rng = np.random.default_rng(8)
-    _check_sampled_dense(w, q, k, v, o, lse, [(0, 0), (0, 31), (1, 17), (1, 31)], rng)
+    check_all_heads_dense(q, k, v, o, lse, w.softmax_scale, w.causal, w.window_left,
+                          w.window_right, w.torch_dtype, w.name)
 
 
-def test_workload_dense_fp16_d512_n4096_sampled():
+def test_workload_dense_fp16_d512_n4096_full():
     w, q, k, v = _dense_workload("dense_fp16_d512_n4096")
     _announce(w.name)
     o, lse = gpu_dense(q, k, v, w.causal)
-    o, lse = o.cpu(), lse.cpu()
     _check_finite(o, lse)
-    rng = np.random.default_rng(9)
-    _check_sampled_dense(w, q, k, v, o, lse, [(0, 0), (0, 5), (0, 7)], rng)
+    check_all_heads_dense(q, k, v, o, lse, w.softmax_scale, w.causal, w.window_left,
+                          w.window_right, w.torch_dtype, w.name)
 
 
-def test_workload_varlen_bf16_d64_w1024_sampled():
+def test_workload_varlen_bf16_d64_w1024_full():
     w = inputs.WORKLOADS["varlen_bf16_d64_w1024"]
     _announce(w.name)
     q, k, v, cu = inputs.make_workload(w)
     o, lse = gpu_varlen(q, k, v, cu, w.causal, w.window_left, w.window_right)
-    o, lse = o.cpu(), lse.cpu()
     _check_finite(o, lse)
-    rng = np.random.default_rng(10)
-    cu_np = cu.numpy()
-    idx = []
-    for s in range(w.num_seqs):
-        a, b = int(cu_np[s]), int(cu_np[s + 1])
-        h = int(rng.integers(0, w.heads))
-        idx += [(h, a + r) for r in sample_rows(b - a, rng, extra=3)]
-    idx = np.array(idx)
-    o_ref, lse_ref = oracle.attention_rows_varlen(q.float(), k.float(), v.float(), cu_np, idx,
-                                                  w.softmax_scale, w.causal, w.window_left,
-                                                  w.window_right)
-    assert_close(to64(o[idx[:, 0], idx[:, 1]]), to64(lse[idx[:, 0], idx[:, 1]]), o_ref,
-                 lse_ref, w.torch_dtype, w.name)
+    check_all_heads_varlen(q, k, v, cu, o, lse, w.softmax_scale, w.causal, w.window_left,
+                           w.window_right, w.torch_dtype, w.name)
 
 
 # ---------------------------------------------------------------------------------------------
