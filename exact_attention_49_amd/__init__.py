@@ -10,13 +10,15 @@ error.
 """
 
 from .binding import (AttnError, attn_bwd, attn_bwd_varlen, attn_fwd,  # noqa: F401
-                      bwd_workspace_size, varlen_bwd_workspace_size, attn_fwd_fp8, attn_fwd_gqa, attn_fwd_splitkv, attn_fwd_varlen,
+                      bwd_workspace_size, varlen_bwd_workspace_size, attn_fwd_fp8, attn_fwd_gqa, attn_fwd_splitkv,
+                      attn_fwd_splitkv_noalloc, attn_fwd_varlen,
                       attn_fwd_varlen_fp8, attn_fwd_varlen_gqa, attn_fwd_varlen_splitkv,
                       library_path, load_library, splitkv_num_splits, splitkv_workspace_size,
                       varlen_splitkv_num_splits, varlen_splitkv_workspace_size)
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
-           "attn_fwd_splitkv", "attn_fwd_varlen_splitkv", "splitkv_num_splits",
+           "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_varlen_splitkv",
+           "splitkv_num_splits",
            "splitkv_workspace_size", "varlen_splitkv_num_splits",
            "varlen_splitkv_workspace_size", "attn_fwd_fp8", "attn_fwd_varlen_fp8", "attn_bwd",
            "attn_bwd_varlen", "bwd_workspace_size", "varlen_bwd_workspace_size",

@@ -15,7 +15,7 @@ import threading
 import torch
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
-           "attn_fwd_splitkv",
+           "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "attn_bwd",
            "attn_bwd_varlen", "bwd_workspace_size", "varlen_bwd_workspace_size", "attn_fwd_fp8",
@@ -33,7 +33,10 @@ STATUS = {
     4: "ATTN_ERR_MISALIGNED",
     5: "ATTN_ERR_TOO_LARGE",
     6: "ATTN_ERR_HIP",
+    7: "ATTN_ERR_SCRATCH_LIMIT",
 }
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 # (name, restype, argtypes) for every function include/exact_attn.h declares
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -48,6 +51,8 @@ EXPORTED_SYMBOLS = {
                               _P, _S, _P]),
     "attn_fwd_varlen_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                      _I, _I, _I, _I, _P, _S, _P]),
+    "attn_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                                      _I, _I, _P]),
     "attn_fwd_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
@@ -321,6 +326,26 @@ def attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
                               ws.numel() * ws.element_size() if ws is not None else 0,
                               _stream_handle(q.device))
     _check(st, "attn_fwd_splitkv")
+    return out, lse
+
+
+def attn_fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             causal: bool = False, window_left: int = -1,
+                             window_right: int = -1, softmax_scale: float | None = None,
+                             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                             return_lse: bool = True, num_splits: int = 0):
+    """attn_fwd_splitkv with the split partials in the library's static per-GPU scratch
+    (ATTN_NOALLOC_SCRATCH_BYTES) instead of a workspace.  The library call allocates nothing;
+    pass `out` (and `lse`, or return_lse=False) to keep this wrapper from allocating too."""
+    bsz, nh, hkv, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
+                                                      return_lse, grouped=True)
+    lib = load_library()
+    st = lib.attn_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None, bsz, nh, hkv,
+                                      n, d, DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                                      int(window_left), int(window_right), int(num_splits),
+                                      _stream_handle(q.device))
+    _check(st, "attn_fwd_splitkv_noalloc")
     return out, lse
 
 

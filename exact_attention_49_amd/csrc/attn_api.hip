@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "exact_attn.h"
 #include "attn_bwd.h"
@@ -26,6 +27,12 @@ template <> hipError_t launch_merge<512>(const MergeArgs&, bool, hipStream_t);
 template <> hipError_t launch_bwd<64>(const BwdArgs&, bool, int, int, int, hipStream_t);
 template <> hipError_t launch_bwd<128>(const BwdArgs&, bool, int, int, int, hipStream_t);
 }  // namespace xattn
+
+// Scratch memory of attn_fwd_splitkv_noalloc: the split partial outputs and their LSE, in a
+// device array of fixed size that the library owns (one copy per GPU, held until the process
+// ends).  In host code `scratch` only names the symbol: its device address on each GPU comes
+// from hipGetSymbolAddress (scratch_address below) and is the only form passed to kernels.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -319,6 +326,37 @@ int run_split(Plan& p, int head_dim, int dtype, int num_splits, void* workspace,
   return launch_split(head_dim, p.a, m, dtype, p.mode, p.n_work, stream);
 }
 
+// ---- allocation-free split-KV --------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that runs `stream` (the current device for the null
+// stream), looked up once per device with that device current and cached.
+int scratch_address(void* stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev)
+                        : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e != hipSuccess) return hip_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_status(e);
+    if (e2 != hipSuccess) return hip_status(e2);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
+
 // ---- backward ---------------------------------------------------------------------------
 
 bool bwd_head_dim(int d) { return d == 64 || d == 128; }
@@ -472,6 +510,26 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   return run_split(p, head_dim, dtype, s, workspace, workspace_size, stream);
 }
 
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int batch, int heads, int heads_kv, int seqlen, int head_dim,
+                             int dtype, float softmax_scale, int causal, int window_left,
+                             int window_right, int num_splits, void* stream) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
+                      softmax_scale, causal, window_left, window_right, 0);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  if (s == 1)  // the plain kernels need no scratch
+    return attn_fwd_gqa(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
+                        softmax_scale, causal, window_left, window_right, stream);
+  if (workspace_bytes_for(p.rows, head_dim, s) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return ATTN_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int st = scratch_address(stream, &ws);
+  if (st != ATTN_OK) return st;
+  return run_split(p, head_dim, dtype, s, ws, ATTN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
                                        int heads, int head_dim) {
   if (num_seqs <= 0 || max_seqlen <= 0 || total_tokens <= 0 || heads <= 0 ||
@@ -617,6 +675,9 @@ const char* attn_status_string(int status) {
       return "ATTN_ERR_MISALIGNED: q/k/v/o need 16-byte, lse/cu_seqlens 4-byte alignment";
     case ATTN_ERR_TOO_LARGE: return "ATTN_ERR_TOO_LARGE: problem exceeds index limits";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error at launch";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "ATTN_ERR_SCRATCH_LIMIT: the split partials exceed the 64 MiB static scratch of "
+             "attn_fwd_splitkv_noalloc (use attn_fwd_splitkv with a workspace, or fewer splits)";
     default: return "unknown status";
   }
 }

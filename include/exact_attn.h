@@ -60,7 +60,8 @@ enum {
   ATTN_ERR_UNSUPPORTED_DTYPE = 3,    /* dtype not fp16 / bf16                               */
   ATTN_ERR_MISALIGNED = 4,           /* q/k/v/o not 16-byte or lse/cu_seqlens not 4-byte    */
   ATTN_ERR_TOO_LARGE = 5,            /* a size would overflow the kernel's index arithmetic */
-  ATTN_ERR_HIP = 6                   /* the HIP runtime reported an error at launch         */
+  ATTN_ERR_HIP = 6,                  /* the HIP runtime reported an error at launch         */
+  ATTN_ERR_SCRATCH_LIMIT = 7         /* attn_fwd_splitkv_noalloc: partials exceed its scratch */
 };
 
 /*
@@ -159,9 +160,33 @@ int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o
                             int window_right, int num_splits, void* workspace,
                             size_t workspace_size, void* stream);
 
+/*
+ * attn_fwd_splitkv_noalloc - attn_fwd_splitkv for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes
+ * no workspace: the split partials live in a device array of ATTN_NOALLOC_SCRATCH_BYTES that
+ * the library owns, one per GPU, held until the process ends.  The call itself makes no
+ * hipMalloc, hipFree or other allocating call; the caller passes inputs and outputs.
+ *   - Arguments, layouts, num_splits and results are those of attn_fwd_splitkv; outputs are
+ *     bitwise equal to attn_fwd_splitkv's for the same split count.
+ *   - ATTN_ERR_SCRATCH_LIMIT when the partials (num_splits x rows x (head_dim + 1) x 4 bytes,
+ *     each part 256-byte aligned; attn_fwd_splitkv_workspace_size gives the figure) exceed
+ *     ATTN_NOALLOC_SCRATCH_BYTES.  Nothing is launched then.  With one split (chosen or
+ *     given) the plain kernels run and the scratch is not touched.
+ *   - The scratch belongs to the GPU that runs `stream` (the current device for the null
+ *     stream); its address is looked up on the first call there.  Every call on one GPU uses
+ *     the same scratch: two calls in flight on that GPU at once (different streams, or host
+ *     threads) race on it and give wrong results.  Calls ordered on one stream are safe.
+ *     Nothing in the scratch needs clearing: each call writes every entry it reads.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int batch, int heads, int heads_kv, int seqlen, int head_dim,
+                             int dtype, float softmax_scale, int causal, int window_left,
+                             int window_right, int num_splits, void* stream);
+
 /* Workspace bytes the split-KV calls need for these sizes (heads = query heads) and
- * num_splits (0 = the count the library would choose).  0 when no workspace is needed (one split) or the arguments are
- * invalid.  Host-only: no device is touched. */
+ * num_splits (0 = the count the library would choose).  0 when no workspace is needed (one
+ * split) or the arguments are invalid.  Host-only: no device is touched. */
 size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
                                        int num_splits);
 size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int total_tokens,
