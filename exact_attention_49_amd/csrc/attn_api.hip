@@ -1,6 +1,7 @@
 // C ABI of the exact-attention forward library: argument validation, kernel selection and
 // launch.  Declared in include/exact_attn.h.  Validation runs entirely on the host and before
 // any HIP call, so a rejected call touches neither the device nor the stream.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -84,17 +85,61 @@ int hip_status(hipError_t e) {
   return ATTN_ERR_HIP;
 }
 
+constexpr int kMaxDevices = 64;
+// Compute units assumed when the runtime cannot say (MI355X has 256).
+constexpr int kDefaultCUs = 256;
+
+// Compute units of HIP device `dev` (the current device for dev < 0), cached per device; the
+// default count if the runtime cannot tell.  Host-side query only.
+int device_cus(int dev = -1) {
+  static std::atomic<int> cache[kMaxDevices];
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  if (dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = kDefaultCUs;
+    cache[dev].store(cus, std::memory_order_relaxed);
+    v = cus;
+  }
+  return v;
+}
+
+// The device a launch on `stream` runs on (the current device for the null stream), or -1.
+int stream_device(void* stream) {
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev)
+                              : hipGetDevice(&dev);
+  return e == hipSuccess ? dev : -1;
+}
+
 int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big, long n_work,
            void* stream) {
   if (n_work <= 0) return ATTN_OK;
   if (n_work > std::numeric_limits<int>::max()) return ATTN_ERR_TOO_LARGE;
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  xattn::FwdArgs b = a;
+  long grid = n_work;
+  if (big && head_dim == 128) {
+    // the ping-pong kernel is persistent: one workgroup per compute unit (the shape fills a
+    // CU), each sweeping a list of the n_work q-tile slots
+    b.n_slots = (int)n_work;
+    const long cus = device_cus(stream_device(stream));
+    grid = n_work < cus ? n_work : cus;
+    // each workgroup's list must fit its LDS item table: the slots split into 8 XCD ranges of
+    // at most ceil(n_work / 8), shared by the XCD's workgroups
+    const long per_xcd = (n_work + 7) / 8;
+    const long wg_per_xcd = (per_xcd + xattn::PP_MAX_ITEMS - 1) / xattn::PP_MAX_ITEMS;
+    if (grid < 8 * wg_per_xcd) grid = 8 * wg_per_xcd;
+  }
   switch (head_dim) {
-    case 64: return hip_status(xattn::launch_fwd<64>(a, bf16, mode, big, (int)n_work, s));
-    case 128: return hip_status(xattn::launch_fwd<128>(a, bf16, mode, big, (int)n_work, s));
-    case 256: return hip_status(xattn::launch_fwd<256>(a, bf16, mode, big, (int)n_work, s));
-    default: return hip_status(xattn::launch_fwd<512>(a, bf16, mode, big, (int)n_work, s));
+    case 64: return hip_status(xattn::launch_fwd<64>(b, bf16, mode, big, (int)grid, s));
+    case 128: return hip_status(xattn::launch_fwd<128>(b, bf16, mode, big, (int)grid, s));
+    case 256: return hip_status(xattn::launch_fwd<256>(b, bf16, mode, big, (int)grid, s));
+    default: return hip_status(xattn::launch_fwd<512>(b, bf16, mode, big, (int)grid, s));
   }
 }
 
@@ -128,10 +173,9 @@ constexpr long kMaxRows = 1L << 40;  // rows * head_dim stays far inside int64
 // The kernels address one sequence's K/V rows with 32-bit byte offsets (buffer loads).
 constexpr long kMaxSeqBytes = (1L << 31) - 1;
 constexpr int kMaxSplits = 64;
-// MI355X: 256 compute units.  Workgroups of the small shape resident per CU at once: four at
-// d = 64, two at d = 128 (register-bound), one for the wide head dims (LDS-bound).  (Measured
-// on B1 H2 N16384 d64 causal: 4 splits 168 us, 3 splits 171 us.)
-constexpr int kNumCUs = 256;
+// Workgroups of the small shape resident per CU at once: four at d = 64, two at d = 128
+// (register-bound), one for the wide head dims (LDS-bound).  (Measured on MI355X, B1 H2 N16384
+// d64 causal: 4 splits 168 us, 3 splits 171 us.)
 int resident_per_cu(int d) { return d == 64 ? 4 : d == 128 ? 2 : 1; }
 // Keys per K/V tile of the small shape.
 int small_tile_keys(int d) { return d >= 256 ? xattn::WideShape::BC : 64; }
@@ -197,20 +241,6 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   a.num_splits = 1;
   a.max_seqlen = seqlen;
   p.n_work = (long)batch * heads * a.tiles_per_head;
-  // Dense causal ping-pong grids run q-tiles m and tiles - 1 - m in one workgroup: every
-  // workgroup of a head then does the same work, so a head's workgroups start and finish
-  // together and stream its K/V in step (B2 H32 N8192 d128: 1067 -> 1045 us).  All pairs cost
-  // the same, so the last round is only full when the pairs fill whole rounds of CUs: fold
-  // only when that fill is at least 95% (B2 H8 N6144, 192 pairs on 256 CUs: 8% slower).
-  a.fold = 0;
-  if (p.big && head_dim == 128 && p.mode == xattn::MASK_CAUSAL) {
-    const long pairs = (long)batch * heads * ((a.tiles_per_head + 1) / 2);
-    const long rounds = (pairs + kNumCUs - 1) / kNumCUs;
-    if (pairs * 20 >= rounds * kNumCUs * 19) {
-      a.fold = 1;
-      p.n_work = pairs;
-    }
-  }
   p.max_len = seqlen;
   return p;
 }
@@ -286,7 +316,7 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
 // in merge traffic and per-workgroup set-up than they gain); 1 when the plain grid already
 // fills the chip.  Chosen by measurement on MI355X over dense and causal shapes.
 int auto_splits(long n_work, int max_len, int head_dim) {
-  const long target = (long)kNumCUs * resident_per_cu(head_dim);
+  const long target = (long)device_cus() * resident_per_cu(head_dim);
   if (n_work <= 0 || n_work >= target) return 1;
   const int tiles = (max_len + small_tile_keys(head_dim) - 1) / small_tile_keys(head_dim);
   long s = (target + n_work - 1) / n_work;
@@ -328,7 +358,6 @@ int run_split(Plan& p, int head_dim, int dtype, int num_splits, void* workspace,
 
 // ---- allocation-free split-KV --------------------------------------------------------------
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch[kMaxDevices] = {};
 

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace xattn {
@@ -73,8 +74,8 @@ struct FwdArgs {
   long split_rows;            // rows of one split's partial arrays (= rows of o)
   float* o_part;              // [num_splits][split_rows][D]
   float* lse_part;            // [num_splits][split_rows], natural log
-  // dense causal ping-pong launches only: the grid covers pairs of q-tiles (m, tiles - 1 - m)
-  int fold;
+  // persistent launches: work slots of the sweep (the grid is smaller and loops over them)
+  int n_slots;
   // packed batches: the caller's bound on every sequence length (the grid is sized from it)
   int max_seqlen;
 };
@@ -338,19 +339,13 @@ __device__ __forceinline__ void fill_malformed_fwd(const FwdArgs& a, const Work&
   }
 }
 
-// Map this workgroup to (q-tile, head, batch | sequence) and, in split-KV mode, a split.
+// Map work slot `wid` of a sweep of `nslots` slots to (q-tile, head, batch | sequence).
 // Dense batches: heads of all batch entries in order with the q-tiles of a head consecutive;
 // masked modes, whose later q-tiles see more keys, instead run each group of heads tile-major,
 // heaviest first.  Packed batches: the q-tile slots of a head walk the sequences in order;
 // slots past the last tile are unused (Skip).
-template <int BR, int MODE, bool SPLIT = false>
-__device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
-  int wid = xcd_remap(blockIdx.x, gridDim.x);
-  w.split = 0;
-  if constexpr (SPLIT) {  // the splits of one q-tile are neighbours (they share its Q rows)
-    w.split = wid % a.num_splits;
-    wid /= a.num_splits;
-  }
+template <int BR, int MODE>
+__device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int nslots, Work& w) {
   const int per = a.tiles_per_head;
   if (a.cu_seqlens == nullptr) {
     int bh, t;
@@ -358,13 +353,13 @@ __device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
       // Masked q-tiles differ in cost (a causal tile m sees m + 1 key tiles).  The (batch,
       // head) pairs are cut into groups of G, inside which the order is tile-major, heaviest
       // first.  G is chosen so that a group holds at least 32 q-tiles (one per CU of an XCD)
-      // but no more pairs than an XCD's share of the grid: with a few tiles per head, a
+      // but no more pairs than an XCD's share of the slots: with a few tiles per head, a
       // head-by-head order would start some heads' heaviest tiles last and leave an XCD on a
       // long tail; with many, one head's tiles already fill the XCD, and all of them stream
       // the same K/V through its L2 together.  With grouped K/V heads a group also holds at
       // least the query heads of one K/V head, so that their tiles run side by side on the
       // same K/V instead of one head after another (B2 Hq32 Hkv8 N8192 causal: 1035 -> 1000 us).
-      const int nbh = (SPLIT ? gridDim.x / a.num_splits : gridDim.x) / per;
+      const int nbh = nslots / per;
       const int G = min((nbh + 7) / 8, max(a.kv_group, (32 + per - 1) / per));
       const int g = wid / (G * per);
       const int r = wid - g * G * per;
@@ -397,28 +392,44 @@ __device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
   return d;
 }
 
-// Folded causal grid: workgroup -> (batch, head) and the q-tile pair (tiles - 1 - m, m), whose
-// two tiles together see tiles + 1 key tiles, so every workgroup of a head does the same work.
-// Same grouped order as decode_work, over pairs.  `light` is m, or -1 when the pair is the
-// middle tile of an odd count.
-template <int BR>
-__device__ __forceinline__ void decode_work_fold(const FwdArgs& a, Work& w, int& light) {
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = a.tiles_per_head, per2 = (per + 1) / 2;
-  const int nbh = gridDim.x / per2;
-  const int G = min((nbh + 7) / 8, max(a.kv_group, (32 + per2 - 1) / per2));
-  const int g = wid / (G * per2);
-  const int r = wid - g * G * per2;
-  const int gsize = min(G, nbh - g * G);
-  const int m = r / gsize;
-  const int bh = g * G + (r - m * gsize);
-  w.tile = per - 1 - m;
-  light = (per - 1 - m != m) ? m : -1;
+// Map this workgroup of a plain grid (one work slot per workgroup, XCD-remapped) to its slot
+// and, in split-KV mode, a split (the splits of one q-tile are neighbours: they share its Q
+// rows).
+template <int BR, int MODE, bool SPLIT = false>
+__device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
+  int wid = xcd_remap(blockIdx.x, gridDim.x);
   w.split = 0;
-  w.seqlen = a.seqlen;
-  w.row0 = (long)bh * a.seqlen;
-  const int b = bh / a.heads_q, h = bh - b * a.heads_q;
-  w.kv_row0 = ((long)b * (a.heads_q / a.kv_group) + h / a.kv_group) * a.seqlen;
+  int nslots = gridDim.x;
+  if constexpr (SPLIT) {
+    w.split = wid % a.num_splits;
+    wid /= a.num_splits;
+    nslots /= a.num_splits;
+  }
+  return decode_slot<BR, MODE>(a, wid, nslots, w);
+}
+
+// Persistent grids: workgroup w runs on XCD w % 8.  The work slots are split into 8 contiguous
+// ranges, one per XCD (as xcd_remap splits a plain grid), and the workgroups of an XCD take
+// its range in rounds, one slot each, alternating direction from round to round.  Slots are
+// ordered heaviest first (decode_slot), so a workgroup's heavy slot of one round is paired with
+// a light one in the next, and all of an XCD's workgroups work on neighbouring slots (the
+// same heads, whose K/V stream through the XCD's L2) at the same time.
+struct Persist {
+  int base, count;  // this XCD's slot range
+  int gx, l;        // workgroups on this XCD and this workgroup's index among them
+};
+__device__ __forceinline__ Persist persist_init(int nslots) {
+  constexpr int NX = 8;
+  const int w = blockIdx.x, P = gridDim.x;
+  const int x = w % NX;
+  const int per = nslots / NX, rem = nslots % NX;
+  return {x * per + min(x, rem), per + (x < rem ? 1 : 0), P / NX + (x < P % NX ? 1 : 0), w / NX};
+}
+// The slot of this workgroup's k-th item, or -1 past its last (rounds are in order, so once a
+// round is past the range every later one is too).
+__device__ __forceinline__ int persist_slot(const Persist& p, int k) {
+  const int local = k * p.gx + ((k & 1) ? p.gx - 1 - p.l : p.l);
+  return local < p.count ? p.base + local : -1;
 }
 
 // Split-KV: restrict the key-tile range [t_lo, t_lo + n) of a q-tile to the share of split
@@ -444,13 +455,19 @@ __device__ __forceinline__ void mode_windows(const FwdArgs& a, int& wl, int& wr)
 // ---------------------------------------------------------------------------------------------
 
 // Q^T operand fragments: lane holds query `row`, d = 16 c + 8 hh .. + 7 (zeros past the end).
+// load_q_nowait issues the loads only (their data is waited for where it is first used).
 template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* qp, int row, int seqlen, int hh,
-                                       i32x4 (&qf)[D / 16]) {
+__device__ __forceinline__ void load_q_nowait(const uint16_t* qp, int row, int seqlen, int hh,
+                                              i32x4 (&qf)[D / 16]) {
   const i32x4* src = (const i32x4*)(qp + (long)row * D);
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
     qf[c] = (row < seqlen) ? src[2 * c + hh] : (i32x4){0, 0, 0, 0};
+}
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* qp, int row, int seqlen, int hh,
+                                       i32x4 (&qf)[D / 16]) {
+  load_q_nowait<D>(qp, row, seqlen, hh, qf);
   // Consume the fragments here, so the wait for these loads sits before the K/V sweep instead
   // of inside it (where it would also wait for tile loads still in flight).
 #pragma unroll
@@ -570,23 +587,33 @@ __device__ __forceinline__ void mma_scores(const char* kt, const LaneOffsets<D>&
 
 // Set invisible scores to -inf: key k0 + (tile position) against query qrow.  Register r of
 // block kb holds tile offset c = 32 kb + 8 (r / 4) + 4 hh + r % 4; the lane's visible offsets
-// form one range [lo, hi] (the key bounds of the row, clipped to the sequence), so each score
-// takes one clamp and one compare: c is visible iff clamp(c, lo, hi) == c.
+// form one range [lo, hi] (the key bounds of the row, clipped to the sequence).  Each edge of
+// the range is applied only when it falls inside the tile for some lane of the wave, as three
+// VALU operations per score: t = hi - c (or c - lo) is negative exactly for the masked scores,
+// its sign spread over the word (t >> 31) selects the bits of -inf (a bitfield insert), and no
+// lane mask registers are needed.
 template <int BC>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[BC / 32], int k0, int qrow, int seqlen,
                                             int wl, int wr, int hh) {
+  constexpr int CMAX = BC - 5;  // the largest offset a lane holds: 32 (BC / 32 - 1) + 24 + 3
+  constexpr unsigned NEG_INF = 0xff800000u;
   const int base = k0 + 4 * hh;
-  int lo = wl >= 0 ? qrow - wl - base : -(1 << 30);
   int hi = seqlen - 1 - base;
   if (wr >= 0) hi = min(hi, qrow + wr - base);
-  if (lo > hi) lo = hi = -(1 << 30);  // nothing visible: no offset c >= 0 survives the clamp
+  const int lo = wl >= 0 ? qrow - wl - base : 0;  // offsets are >= 0: lo <= 0 clips nothing
+  auto edge = [&](auto right) XATTN_INLINE {
 #pragma unroll
-  for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-      if (min(max(c, lo), hi) != c) s[kb][r] = -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+        const int t = decltype(right)::value ? hi - c : c - lo;
+        const unsigned m = (unsigned)(t >> 31);  // all ones where masked
+        s[kb][r] = __uint_as_float((m & NEG_INF) | (~m & __float_as_uint(s[kb][r])));
+      }
+  };
+  if (__builtin_amdgcn_ballot_w64(hi < CMAX) != 0) edge(std::true_type{});
+  if (__builtin_amdgcn_ballot_w64(lo > 0) != 0) edge(std::false_type{});
 }
 
 // Online softmax of one tile (base 2) with a lazily moved reference max.  Turns the scores

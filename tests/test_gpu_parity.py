@@ -116,8 +116,8 @@ def test_workload_causal_bf16_d128_n2048_full():
 
 
 def test_workload_causal_bf16_d128_n8192_full():
-    """Every row of all 64 (batch, head) pairs (the benchmark's launch: folded ping-pong
-    grid)."""
+    """Every row of all 64 (batch, head) pairs (the benchmark's launch: the persistent
+    ping-pong kernel)."""
     w, q, k, v = _dense_workload("causal_bf16_d128_n8192")
     _announce(w.name)
     o, lse = gpu_dense(q, k, v, w.causal)
@@ -244,12 +244,12 @@ def test_pingpong_masked_grid_with_partial_last_group():
                      f"head {hd}")
 
 
-def test_pingpong_folded_causal_odd_tile_count():
-    """B1 H256 N2304 d128 causal: 9 q-tiles of 256 rows per head, run as folded pairs
-    (8, 0), (7, 1), (6, 2), (5, 3) and the middle tile 4 alone; 1280 pairs fill five rounds of
-    256 CUs.  Work-order groups of 7 heads end in a group of 4.  Heads from the first, a middle
-    and the last group are compared with the oracle in full."""
-    _announce("ping-pong folded causal B1 H256 N2304")
+def test_pingpong_causal_odd_tile_count():
+    """B1 H256 N2304 d128 causal: 9 q-tiles of 256 rows per head (2304 slots, 9 per workgroup
+    of the persistent grid, whose rounds alternate direction so that heavy and light tiles
+    pair up).  Work-order groups of 7 heads end in a group of 4.  Heads from the first, a
+    middle and the last group are compared with the oracle in full."""
+    _announce("ping-pong causal B1 H256 N2304")
     q, k, v = inputs.make_dense(1, 256, 2304, 128, "bf16", seed=360)
     o, lse = gpu_dense(q, k, v, True)
     for hd in (0, 6, 7, 130, 251, 252, 255):

@@ -1,5 +1,5 @@
 """GPU parity of the d = 128 ping-pong kernel in the configurations the other tests reach
-only with bf16 or one-sided masks: fp16 I/O (unmasked, causal on a folded grid, causal with a
+only with bf16 or one-sided masks: fp16 I/O (unmasked, causal, causal with a
 left window) and two-sided windows with causal = 0 (both dtypes).  Every grid here is large
 enough for the library to pick the ping-pong kernel (256 unmasked / 384 masked 256-row tiles;
 the host mirror of that choice in bench.py is asserted first), and every row of every head is
@@ -24,8 +24,8 @@ DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 CASES = {
     # 256 unmasked tiles
     "fp16_none_b1h32n2048": (1, 32, 2048, "fp16", False, -1, -1, 1.0),
-    # 1024 causal tiles folded into 512 pairs, two whole rounds of 256 CUs
-    "fp16_causal_folded_b2h32n4096": (2, 32, 4096, "fp16", True, -1, -1, 0.5),
+    # 1024 causal tiles, four per workgroup of the persistent grid
+    "fp16_causal_b2h32n4096": (2, 32, 4096, "fp16", True, -1, -1, 0.5),
     # 384 tiles under a causal mask with a left window (window mask mode)
     "fp16_causal_w300_b1h48n2048": (1, 48, 2048, "fp16", True, 300, -1, 1.0),
     # two-sided windows without causal, 384 and 512 tiles
