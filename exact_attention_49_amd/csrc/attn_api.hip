@@ -85,6 +85,7 @@ int hip_status(hipError_t e) {
   return ATTN_ERR_HIP;
 }
 
+long varlen_slots(int rows, int num_seqs, int max_seqlen, int total_tokens);
 constexpr int kMaxDevices = 64;
 // Compute units assumed when the runtime cannot say (MI355X has 256).
 constexpr int kDefaultCUs = 256;
@@ -124,6 +125,28 @@ int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big,
   xattn::FwdArgs b = a;
   long grid = n_work;
   if (big && head_dim == 128) {
+    // Grouped K/V heads: the query heads of a K/V head share each K/V tile in one q-tile
+    // (pack of them, the largest power of two dividing the group, at most 8: one wave of 32
+    // positions per head at least), which then holds 256 / pack positions of each.
+    int pack = 1;
+    while (pack < 8 && a.kv_group % (2 * pack) == 0) pack *= 2;
+    if (pack > 1) {
+      const int rows = xattn::PingPongShape::BR / pack;
+      const long pseudo = a.heads_q / pack;  // packed groups of query heads
+      long per;
+      if (a.cu_seqlens == nullptr) {
+        const long batch = n_work / ((long)a.heads_q * a.tiles_per_head);
+        per = (a.seqlen + rows - 1) / rows;
+        n_work = batch * pseudo * per;
+      } else {
+        per = varlen_slots(rows, a.num_seqs, a.max_seqlen, a.total_tokens);
+        n_work = pseudo * per;
+      }
+      if (per > std::numeric_limits<int>::max() || n_work > std::numeric_limits<int>::max())
+        return ATTN_ERR_TOO_LARGE;
+      b.tiles_per_head = (int)per;
+      b.pack = pack;
+    }
     // the ping-pong kernel is persistent: one workgroup per compute unit (the shape fills a
     // CU), each sweeping a list of the n_work q-tile slots
     b.n_slots = (int)n_work;
@@ -239,6 +262,7 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   a.heads_q = heads;
   a.kv_group = heads / heads_kv;
   a.num_splits = 1;
+  a.pack = 1;
   a.max_seqlen = seqlen;
   p.n_work = (long)batch * heads * a.tiles_per_head;
   p.max_len = seqlen;
@@ -305,6 +329,7 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
   a.heads_q = heads;
   a.kv_group = heads / heads_kv;
   a.num_splits = 1;
+  a.pack = 1;
   a.max_seqlen = max_seqlen;
   p.n_work = (long)heads * slots;
   p.max_len = max_seqlen;

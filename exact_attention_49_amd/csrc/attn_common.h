@@ -76,6 +76,9 @@ struct FwdArgs {
   float* lse_part;            // [num_splits][split_rows], natural log
   // persistent launches: work slots of the sweep (the grid is smaller and loops over them)
   int n_slots;
+  // persistent launches: query heads of one K/V head packed into one q-tile (1: none); a
+  // q-tile then holds BR / pack positions of each of them
+  int pack;
   // packed batches: the caller's bound on every sequence length (the grid is sized from it)
   int max_seqlen;
 };
@@ -270,6 +273,7 @@ struct Work {
   long kv_row0;  // the same for k/v (differs from row0 with grouped K/V heads)
   int split;   // split-KV: which share of the q-tile's key tiles (0 otherwise)
   int bad_lo, bad_hi;  // Decoded::Malformed only: the sequence rows to fill with NaN
+  int c0;      // the sequence's first token (0 for a dense batch)
 };
 
 // What a workgroup's slot decodes to: nothing (a slot past the last tile), a tile to compute,
@@ -344,8 +348,10 @@ __device__ __forceinline__ void fill_malformed_fwd(const FwdArgs& a, const Work&
 // masked modes, whose later q-tiles see more keys, instead run each group of heads tile-major,
 // heaviest first.  Packed batches: the q-tile slots of a head walk the sequences in order;
 // slots past the last tile are unused (Skip).
+// (`rows`: rows per q-tile, BR unless the caller packs several heads into a tile.)
 template <int BR, int MODE>
-__device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int nslots, Work& w) {
+__device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int nslots, Work& w,
+                                               int rows = BR) {
   const int per = a.tiles_per_head;
   if (a.cu_seqlens == nullptr) {
     int bh, t;
@@ -377,18 +383,20 @@ __device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int ns
     // they run on the same XCD and share its L2 copy of the K/V head
     const int b = bh / a.heads_q, h = bh - b * a.heads_q;
     w.kv_row0 = ((long)b * (a.heads_q / a.kv_group) + h / a.kv_group) * a.seqlen;
+    w.c0 = 0;
     return Decoded::Run;
   }
   const int h = wid / per;
   const int slot = wid - h * per;
   int c0, len, t, nt;
-  const Decoded d = find_seq_tile(a, slot, BR, c0, len, t, nt);
+  const Decoded d = find_seq_tile(a, slot, rows, c0, len, t, nt);
   if (d == Decoded::Skip) return d;
   w.tile = (MODE != MASK_NONE) ? nt - 1 - t : t;
   w.seqlen = len;
   w.row0 = (long)h * a.total_tokens + c0;
   w.kv_row0 = (long)(h / a.kv_group) * a.total_tokens + c0;
-  if (d == Decoded::Malformed) malformed_rows(t, nt, BR, len, w.bad_lo, w.bad_hi);
+  w.c0 = c0;
+  if (d == Decoded::Malformed) malformed_rows(t, nt, rows, len, w.bad_lo, w.bad_hi);
   return d;
 }
 

@@ -122,12 +122,20 @@ __device__ __forceinline__ void pp_build_table(const FwdArgs& a, const Persist& 
     if (__builtin_amdgcn_ballot_w64(slot >= 0) == 0) break;
     Work w;
     w.split = 0;
-    const Decoded d = slot >= 0 ? decode_slot<BR, MODE>(a, slot, a.n_slots, w) : Decoded::Skip;
+    // with packing, a slot is one group of `pack` query heads of a K/V head ("pseudo-head") and
+    // P positions of each
+    FwdArgs ap = a;
+    ap.heads_q = a.heads_q / a.pack;
+    ap.kv_group = a.kv_group / a.pack;
+    const int P = BR / a.pack;
+    const Decoded d = slot >= 0 ? decode_slot<BR, MODE>(ap, slot, a.n_slots, w, P)
+                                : Decoded::Skip;
+    w.row0 = (long)a.pack * (w.row0 - w.c0) + w.c0;  // the group's first query head
     const bool run = d == Decoded::Run, bad = d == Decoded::Malformed;
     int n = 0, t_lo = 0;
     if (run) {
-      const int q0 = w.tile * BR;
-      const int q_last = min(q0 + BR, w.seqlen) - 1;  // last valid row of the tile
+      const int q0 = w.tile * P;
+      const int q_last = min(q0 + P, w.seqlen) - 1;  // last valid position of the tile
       int k_lo = 0, k_hi = w.seqlen - 1;              // keys any valid row can see
       if (wl >= 0) k_lo = max(0, q0 - wl);
       if (wr >= 0) k_hi = min(w.seqlen - 1, q_last + wr);
@@ -148,7 +156,7 @@ __device__ __forceinline__ void pp_build_table(const FwdArgs& a, const Persist& 
       const int k = base + __builtin_popcountl(mrun & below);
       if (k < PP_MAX_ITEMS) {
         t.item[3 * k] = (i32x4){g_acc + incl - n, n, t_lo, w.seqlen};
-        t.item[3 * k + 1] = (i32x4){w.tile * BR, (int)(unsigned)w.row0,
+        t.item[3 * k + 1] = (i32x4){w.tile * P, (int)(unsigned)w.row0,
                                     (int)(unsigned)((unsigned long)w.row0 >> 32),
                                     (int)(unsigned)w.kv_row0};
         t.item[3 * k + 2] = (i32x4){(int)(unsigned)((unsigned long)w.kv_row0 >> 32), 0, 0, 0};
@@ -194,6 +202,12 @@ void attn_fwd_pp_kernel(FwdArgs a) {
   const bool grp_a = wave < 4;
   int wl, wr;
   mode_windows<MODE>(a, wl, wr);
+  // Packed grouped heads (FwdArgs::pack > 1): a q-tile holds `pack` query heads of one K/V
+  // head (the kBlockH packing of page "flash_fwd_kernel.h" @c272619) and BR / pack positions
+  // of each; wave w computes 32 positions of head w / wpp, so every wave uses the same K/V
+  // tiles.  hstride: rows between consecutive query heads.
+  const int wpp = 8 / a.pack;  // waves per head of the q-tile
+  const long hstride = a.cu_seqlens != nullptr ? (long)a.total_tokens : (long)a.seqlen;
 
   // ---- the workgroup's q-tiles and the length of its sweep ------------------------------
   __shared__ PPTable tab;
@@ -210,7 +224,10 @@ void attn_fwd_pp_kernel(FwdArgs a) {
                       (unsigned)__builtin_amdgcn_readfirstlane(e[0]));
       w.bad_lo = __builtin_amdgcn_readfirstlane(e[2]);
       w.bad_hi = __builtin_amdgcn_readfirstlane(e[3]);
-      fill_malformed_fwd<D>(a, w);
+      for (int j = 0; j < a.pack; ++j) {  // every query head of the packed group
+        fill_malformed_fwd<D>(a, w);
+        w.row0 += hstride;
+      }
     }
   }
   if (n_items == 0) return;
@@ -231,7 +248,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
     v.seqlen = it.seqlen;
     v.rk = kv_rsrc(it, true);
     v.rv = kv_rsrc(it, false);
-    const int qw0 = it.q0 + wv * 32;
+    const int qw0 = it.q0 + (wv % wpp) * 32;
     v.qw0 = qw0;
     if (qw0 >= it.seqlen) {  // no row of this wave in the q-tile
       v.vis_lo = v.end;
@@ -277,7 +294,10 @@ void attn_fwd_pp_kernel(FwdArgs a) {
 
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
   i32x4 qf[D / 16];
-  load_q<D>(a.q + first.row0 * D, first.q0 + wave * 32 + l32, first.seqlen, hh, qf);
+  // the rows of this wave's head, and its first position in a q-tile
+  const long hrow = (long)(wv / wpp) * hstride;
+  const int wpos = (wv % wpp) * 32;
+  load_q<D>(a.q + (first.row0 + hrow) * D, first.q0 + wpos + l32, first.seqlen, hh, qf);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -370,9 +390,9 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       const bool in_c = gpv < wcur.end;
       if (gpv == (in_c ? wcur.end : wnxt.end) - 1) {  // the q-tile is done: store it, reset
         const PPItem it = pp_read_item(tab, in_c ? k_cur : k_cur + 1);
-        const int qw0 = it.q0 + wv * 32;
+        const int qw0 = it.q0 + wpos;
         if (qw0 < it.seqlen)
-          store_rows<BF16, D>(a, it.row0, qw0 + l32, it.seqlen, hh, oacc, m_run, l_run);
+          store_rows<BF16, D>(a, it.row0 + hrow, qw0 + l32, it.seqlen, hh, oacc, m_run, l_run);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -399,7 +419,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
     const int it_end = in_c ? wcur.end : wnxt.end;
     if (g == it_end - 1 && g + 1 < total) {
       const PPItem nx = pp_read_item(tab, k_cur + (in_c ? 1 : 2));
-      load_q_nowait<D>(a.q + nx.row0 * D, nx.q0 + wave * 32 + l32, nx.seqlen, hh, qf);
+      load_q_nowait<D>(a.q + (nx.row0 + hrow) * D, nx.q0 + wpos + l32, nx.seqlen, hh, qf);
     }
     const bool vis = sees(g);
     bool spread = false;

@@ -55,3 +55,42 @@ def test_persistent_dense_many_items(shape, causal, dt):
         sl = slice(hd, hd + 1)
         check_all_heads_dense(q[:, sl], k[:, sl], v[:, sl], o[:, sl], lse[:, sl],
                               1 / math.sqrt(128), causal, -1, -1, DTYPES[dt], f"head {hd}")
+
+
+# (B, Hq, Hkv, N): grouped K/V heads on the persistent kernel; the query heads of a K/V head
+# are packed into one q-tile by the largest power of two dividing the group, at most 8:
+# MQA (group 32: 8 heads of 32 positions per q-tile), group 3 (no packing), group 6 (2 heads
+# of 128 positions), group 12 (4 heads of 64 positions, ragged N)
+PACKED = [(1, 32, 1, 4096), (1, 36, 12, 4096), (1, 48, 8, 2048), (2, 24, 2, 2100)]
+PACK_MASKS = {"none": (False, -1, -1), "causal": (True, -1, -1), "window_30_70": (False, 30, 70),
+              "causal_w200": (True, 200, -1)}
+
+
+@pytest.mark.parametrize("mask", list(PACK_MASKS))
+@pytest.mark.parametrize("shape", PACKED)
+def test_packed_heads_match_repeated_kv_and_oracle(shape, mask):
+    """A packed q-tile computes each of its heads' rows with the same key tiles, in the same
+    order, as an unpacked one: the grouped call must equal attn_fwd on K/V repeated along the
+    heads bit for bit, and match the oracle (first, middle and last query head in full)."""
+    from exact_attention_49_amd import attn_fwd, attn_fwd_gqa
+    b, hq, hkv, n = shape
+    causal, wl, wr = PACK_MASKS[mask]
+    print(f"[case] packed heads {shape} {mask}", flush=True)
+    q, k, v = inputs.make_dense(b, hq, n, 128, "bf16", seed=1700 + hq + hkv, heads_kv=hkv)
+    w = inputs.Workload(name="t", heads=hq, heads_kv=hkv, head_dim=128, dtype="bf16",
+                        causal=causal, seed=0, batch=b, seqlen=n, window_left=wl,
+                        window_right=wr)
+    assert bench.kernel_name(w) == "attn_fwd_pp_kernel"
+    o, lse = attn_fwd_gqa(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl,
+                          window_right=wr)
+    g = hq // hkv
+    o2, lse2 = attn_fwd(q.to(DEV), k.repeat_interleave(g, 1).to(DEV),
+                        v.repeat_interleave(g, 1).to(DEV), causal=causal, window_left=wl,
+                        window_right=wr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for hd in sorted({0, hq // 2, hq - 1}):
+        sl = slice(hd, hd + 1)
+        kh = slice(hd // g, hd // g + 1)
+        check_all_heads_dense(q[:, sl], k[:, kh], v[:, kh], o[:, sl], lse[:, sl],
+                              1 / math.sqrt(128), causal, wl, wr, torch.bfloat16, f"head {hd}")
