@@ -64,6 +64,8 @@ KERNEL_SOURCES = {
                            "attn_fwd_d512.hip"),
     "fp8": _SHARED + ("attn_fwd_fp8.h", "attn_fwd_fp8.hip"),
     "bwd": _SHARED + ("attn_bwd.h", "attn_bwd_d64.hip", "attn_bwd_d128.hip"),
+    "persistent": _FWD_SHARED + ("attn_fwd_pingpong.h", "attn_fwd_persistent.h",
+                                 "attn_fwd_pers.hip"),
 }
 
 

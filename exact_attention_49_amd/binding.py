@@ -15,6 +15,7 @@ import threading
 import torch
 
 __all__ = ["AttnError", "attn_fwd", "attn_fwd_varlen", "attn_fwd_gqa", "attn_fwd_varlen_gqa",
+           "attn_fwd_persistent", "attn_fwd_varlen_persistent",
            "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
            "attn_fwd_varlen_splitkv", "splitkv_num_splits", "splitkv_workspace_size",
            "varlen_splitkv_num_splits", "varlen_splitkv_workspace_size", "attn_bwd",
@@ -47,6 +48,10 @@ EXPORTED_SYMBOLS = {
     "attn_fwd_gqa": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "attn_fwd_varlen_gqa": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                  _I, _I, _P]),
+    "attn_fwd_persistent": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                                 _P]),
+    "attn_fwd_varlen_persistent": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                        _F, _I, _I, _I, _P]),
     "attn_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                               _P, _S, _P]),
     "attn_fwd_varlen_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -268,6 +273,46 @@ def attn_fwd_varlen_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  int(bool(causal)), int(window_left), int(window_right),
                                  _stream_handle(q.device))
     _check(st, "attn_fwd_varlen_gqa")
+    return out, lse
+
+
+def attn_fwd_persistent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                        window_left: int = -1, window_right: int = -1,
+                        softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                        lse: torch.Tensor | None = None, return_lse: bool = True):
+    """attn_fwd_gqa on the persistent schedule (head dim 128): q [B, Hq, N, 128], k and v
+    [B, Hkv, N, 128] with Hkv dividing Hq.  Returns (o like q, lse fp32 [B, Hq, N])."""
+    bsz, hq, hkv, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
+                                                      return_lse, grouped=True)
+    lib = load_library()
+    st = lib.attn_fwd_persistent(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, bsz, hq, hkv, n,
+                                 d, DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                                 int(window_left), int(window_right), _stream_handle(q.device))
+    _check(st, "attn_fwd_persistent")
+    return out, lse
+
+
+def attn_fwd_varlen_persistent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = False,
+                               window_left: int = -1, window_right: int = -1,
+                               softmax_scale: float | None = None,
+                               out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                               return_lse: bool = True):
+    """attn_fwd_varlen_gqa on the persistent schedule (head dim 128): q [Hq, total, 128],
+    k and v [Hkv, total, 128]."""
+    hq, hkv, total, d, scale, out, lse = _varlen_args(q, k, v, cu_seqlens, softmax_scale, out,
+                                                      lse, return_lse, grouped=True)
+    lib = load_library()
+    st = lib.attn_fwd_varlen_persistent(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        out.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None,
+                                        cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                        int(max_seqlen), total, hq, hkv, d,
+                                        DTYPE_CODES[q.dtype], scale, int(bool(causal)),
+                                        int(window_left), int(window_right),
+                                        _stream_handle(q.device))
+    _check(st, "attn_fwd_varlen_persistent")
     return out, lse
 
 

@@ -11,6 +11,7 @@
 #include "attn_bwd.h"
 #include "attn_fwd_fp8.h"
 #include "attn_dispatch.h"
+#include "attn_fwd_persistent.h"
 
 namespace xattn {
 template <> hipError_t launch_fwd<64>(const FwdArgs&, bool, int, bool, int, hipStream_t);
@@ -116,6 +117,32 @@ int stream_device(void* stream) {
   return e == hipSuccess ? dev : -1;
 }
 
+// Grouped K/V heads on the ping-pong shape: the query heads of a K/V head share each K/V tile
+// in one q-tile (`pack` of them, the largest power of two dividing the group, at most 8: one
+// wave of 32 positions per head at least), which then holds 256 / pack positions of each.
+// Rewrites the tile count per (packed) head and the work count n_work.
+int pack_heads(xattn::FwdArgs& b, long& n_work) {
+  int pack = 1;
+  while (pack < 8 && b.kv_group % (2 * pack) == 0) pack *= 2;
+  if (pack == 1) return ATTN_OK;
+  const int rows = xattn::PingPongShape::BR / pack;
+  const long groups = b.heads_q / pack;  // packed groups of query heads
+  long per;
+  if (b.cu_seqlens == nullptr) {
+    const long batch = n_work / ((long)b.heads_q * b.tiles_per_head);
+    per = (b.seqlen + rows - 1) / rows;
+    n_work = batch * groups * per;
+  } else {
+    per = varlen_slots(rows, b.num_seqs, b.max_seqlen, b.total_tokens);
+    n_work = groups * per;
+  }
+  if (per > std::numeric_limits<int>::max() || n_work > std::numeric_limits<int>::max())
+    return ATTN_ERR_TOO_LARGE;
+  b.tiles_per_head = (int)per;
+  b.pack = pack;
+  return ATTN_OK;
+}
+
 int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big, long n_work,
            void* stream) {
   if (n_work <= 0) return ATTN_OK;
@@ -125,38 +152,21 @@ int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big,
   xattn::FwdArgs b = a;
   long grid = n_work;
   if (big && head_dim == 128) {
-    // Grouped K/V heads: the query heads of a K/V head share each K/V tile in one q-tile
-    // (pack of them, the largest power of two dividing the group, at most 8: one wave of 32
-    // positions per head at least), which then holds 256 / pack positions of each.
-    int pack = 1;
-    while (pack < 8 && a.kv_group % (2 * pack) == 0) pack *= 2;
-    if (pack > 1) {
-      const int rows = xattn::PingPongShape::BR / pack;
-      const long pseudo = a.heads_q / pack;  // packed groups of query heads
-      long per;
-      if (a.cu_seqlens == nullptr) {
-        const long batch = n_work / ((long)a.heads_q * a.tiles_per_head);
-        per = (a.seqlen + rows - 1) / rows;
-        n_work = batch * pseudo * per;
-      } else {
-        per = varlen_slots(rows, a.num_seqs, a.max_seqlen, a.total_tokens);
-        n_work = pseudo * per;
+    if (const int st = pack_heads(b, n_work); st != ATTN_OK) return st;
+    grid = n_work;
+    // Dense causal grids fold the q-tiles of a head into pairs of equal total work (t, T-1-t)
+    // when the pairs fill their last round of one workgroup per CU at least to 95%: halving
+    // the workgroup count then costs no balance and saves a Q load and a prologue per pair.
+    if (mode == xattn::MASK_CAUSAL && b.cu_seqlens == nullptr) {
+      const long heads = n_work / b.tiles_per_head;  // (batch, packed head) pairs
+      const long pairs = heads * ((b.tiles_per_head + 1) / 2);
+      const long cus = device_cus(stream_device(stream));
+      const long rounds = (pairs + cus - 1) / cus;
+      if (pairs * 20 >= rounds * cus * 19) {
+        b.fold = 1;
+        grid = pairs;
       }
-      if (per > std::numeric_limits<int>::max() || n_work > std::numeric_limits<int>::max())
-        return ATTN_ERR_TOO_LARGE;
-      b.tiles_per_head = (int)per;
-      b.pack = pack;
     }
-    // the ping-pong kernel is persistent: one workgroup per compute unit (the shape fills a
-    // CU), each sweeping a list of the n_work q-tile slots
-    b.n_slots = (int)n_work;
-    const long cus = device_cus(stream_device(stream));
-    grid = n_work < cus ? n_work : cus;
-    // each workgroup's list must fit its LDS item table: the slots split into 8 XCD ranges of
-    // at most ceil(n_work / 8), shared by the XCD's workgroups
-    const long per_xcd = (n_work + 7) / 8;
-    const long wg_per_xcd = (per_xcd + xattn::PP_MAX_ITEMS - 1) / xattn::PP_MAX_ITEMS;
-    if (grid < 8 * wg_per_xcd) grid = 8 * wg_per_xcd;
   }
   switch (head_dim) {
     case 64: return hip_status(xattn::launch_fwd<64>(b, bf16, mode, big, (int)grid, s));
@@ -164,6 +174,26 @@ int launch(int head_dim, const xattn::FwdArgs& a, int dtype, int mode, bool big,
     case 256: return hip_status(xattn::launch_fwd<256>(b, bf16, mode, big, (int)grid, s));
     default: return hip_status(xattn::launch_fwd<512>(b, bf16, mode, big, (int)grid, s));
   }
+}
+
+// The persistent ping-pong kernel (head dim 128, 256-row q-tiles): one workgroup per compute
+// unit, each sweeping its list of the n_work q-tile slots.
+int launch_persistent(const xattn::FwdArgs& a, int dtype, int mode, long n_work, void* stream) {
+  if (n_work <= 0) return ATTN_OK;
+  xattn::FwdArgs b = a;
+  if (const int st = pack_heads(b, n_work); st != ATTN_OK) return st;
+  if (n_work > std::numeric_limits<int>::max()) return ATTN_ERR_TOO_LARGE;
+  b.fold = 0;
+  b.n_slots = (int)n_work;
+  const long cus = device_cus(stream_device(stream));
+  long grid = n_work < cus ? n_work : cus;
+  // each workgroup's list must fit its LDS item table: the slots split into 8 XCD ranges of at
+  // most ceil(n_work / 8), shared by the XCD's workgroups
+  const long per_xcd = (n_work + 7) / 8;
+  const long wg_per_xcd = (per_xcd + xattn::PP_MAX_ITEMS - 1) / xattn::PP_MAX_ITEMS;
+  if (grid < 8 * wg_per_xcd) grid = 8 * wg_per_xcd;
+  return hip_status(xattn::launch_fwd_persistent(b, dtype == ATTN_DTYPE_BF16, mode, (int)grid,
+                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
 // Split-KV: the split sweep (grid = n_work x num_splits) and then the merge.
@@ -215,7 +245,7 @@ struct Plan {
   int max_len = 0;       // longest sequence
 };
 
-// shape: 1 = choose (big if the grid is large enough), 0 = small shape.
+// shape: 1 = choose (big if the grid is large enough), 0 = small shape, 2 = big shape.
 Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                 int heads, int heads_kv, int seqlen, int head_dim, int dtype,
                 float softmax_scale, int causal, int window_left, int window_right, int shape) {
@@ -244,8 +274,8 @@ Plan plan_dense(const void* q, const void* k, const void* v, void* o, float* lse
   int wl = window_left, wr = window_right;
   p.mode = mask_mode(causal, seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);
-  p.big = shape == 1 &&
-          (long)batch * heads * ((seqlen + br_big - 1) / br_big) >= xattn::big_tile_min_work(p.mode);
+  const long big_tiles = (long)batch * heads * ((seqlen + br_big - 1) / br_big);
+  p.big = shape == 2 || (shape == 1 && big_tiles >= xattn::big_tile_min_work(p.mode));
   const int br = block_rows(head_dim, p.big);
   xattn::FwdArgs& a = p.a;
   a.q = static_cast<const uint16_t*>(q);
@@ -304,8 +334,8 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
   int wl = window_left, wr = window_right;
   p.mode = mask_mode(causal, max_seqlen, &wl, &wr);
   const int br_big = block_rows(head_dim, true);
-  p.big = shape == 1 && (long)heads * (((long)total_tokens + br_big - 1) / br_big) >=
-                            xattn::big_tile_min_work(p.mode);
+  const long big_tiles = (long)heads * (((long)total_tokens + br_big - 1) / br_big);
+  p.big = shape == 2 || (shape == 1 && big_tiles >= xattn::big_tile_min_work(p.mode));
   const int br = block_rows(head_dim, p.big);
   // q-tile slots per head: an upper bound on sum_s ceil(len_s / br) that needs no lengths
   const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;
@@ -530,6 +560,30 @@ int attn_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, fl
                        window_right, 1);
   if (p.status != ATTN_OK || p.empty) return p.status;
   return launch(head_dim, p.a, dtype, p.mode, p.big, p.n_work, stream);
+}
+
+int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int batch, int heads_q, int heads_kv, int seqlen, int head_dim,
+                        int dtype, float softmax_scale, int causal, int window_left,
+                        int window_right, void* stream) {
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_dense(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen, head_dim, dtype,
+                      softmax_scale, causal, window_left, window_right, 2);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch_persistent(p.a, dtype, p.mode, p.n_work, stream);
+}
+
+int attn_fwd_varlen_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                               int total_tokens, int heads_q, int heads_kv, int head_dim,
+                               int dtype, float softmax_scale, int causal, int window_left,
+                               int window_right, void* stream) {
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  Plan p = plan_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen, total_tokens,
+                       heads_q, heads_kv, head_dim, dtype, softmax_scale, causal, window_left,
+                       window_right, 2);
+  if (p.status != ATTN_OK || p.empty) return p.status;
+  return launch_persistent(p.a, dtype, p.mode, p.n_work, stream);
 }
 
 int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim) {

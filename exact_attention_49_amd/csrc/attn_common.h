@@ -74,10 +74,12 @@ struct FwdArgs {
   long split_rows;            // rows of one split's partial arrays (= rows of o)
   float* o_part;              // [num_splits][split_rows][D]
   float* lse_part;            // [num_splits][split_rows], natural log
+  // dense causal ping-pong launches only: the grid covers pairs of q-tiles (m, tiles - 1 - m)
+  int fold;
   // persistent launches: work slots of the sweep (the grid is smaller and loops over them)
   int n_slots;
-  // persistent launches: query heads of one K/V head packed into one q-tile (1: none); a
-  // q-tile then holds BR / pack positions of each of them
+  // ping-pong launches: query heads of one K/V head packed into one q-tile (1: none); a q-tile
+  // then holds BR / pack positions of each of them
   int pack;
   // packed batches: the caller's bound on every sequence length (the grid is sized from it)
   int max_seqlen;
@@ -404,7 +406,7 @@ __device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int ns
 // and, in split-KV mode, a split (the splits of one q-tile are neighbours: they share its Q
 // rows).
 template <int BR, int MODE, bool SPLIT = false>
-__device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
+__device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w, int rows = BR) {
   int wid = xcd_remap(blockIdx.x, gridDim.x);
   w.split = 0;
   int nslots = gridDim.x;
@@ -413,7 +415,7 @@ __device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w) {
     wid /= a.num_splits;
     nslots /= a.num_splits;
   }
-  return decode_slot<BR, MODE>(a, wid, nslots, w);
+  return decode_slot<BR, MODE>(a, wid, nslots, w, rows);
 }
 
 // Persistent grids: workgroup w runs on XCD w % 8.  The work slots are split into 8 contiguous

@@ -115,6 +115,9 @@ hipError_t launch_fwd_split(const FwdArgs& a, bool bf16, int mode, int n_work,
                             hipStream_t stream);
 template <int D>
 hipError_t launch_merge(const MergeArgs& m, bool bf16, hipStream_t stream);
+// The persistent ping-pong kernel (head dim 128) over `grid` workgroups (attn_fwd_pers.hip).
+hipError_t launch_fwd_persistent(const FwdArgs& a, bool bf16, int mode, int grid,
+                                 hipStream_t stream);
 
 #define XATTN_DEFINE_LAUNCHER(D)                                                            \
   template <>                                                                               \

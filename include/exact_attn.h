@@ -126,6 +126,29 @@ int attn_fwd_varlen_gqa(const void* q, const void* k, const void* v, void* o, fl
                         void* stream);
 
 /*
+ * Persistent-schedule variants of attn_fwd_gqa / attn_fwd_varlen_gqa for head_dim 128 (any
+ * other head dim gives ATTN_ERR_UNSUPPORTED_HEAD_DIM).  The grid holds one workgroup per
+ * compute unit; each takes a fixed list of 256-row q-tiles and sweeps their key tiles as one
+ * continuous pipeline (the persistent tile scheduler of page "flash_fwd_kernel.h" @26a6e0a,
+ * get_initial_work / get_next_work, with the list fixed at launch).  Arguments, layouts,
+ * results and errors are those of attn_fwd_gqa / attn_fwd_varlen_gqa; outputs agree with
+ * theirs up to rounding (the same arithmetic per q-tile, in a different tile order).  The
+ * default entry points use the hardware's own dispatch of one workgroup per q-tile, which
+ * balances uneven tiles as well or better on MI355X; these are for callers that want the
+ * fixed schedule (a bounded number of resident workgroups).
+ */
+int attn_fwd_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int batch, int heads_q, int heads_kv, int seqlen, int head_dim,
+                        int dtype, float softmax_scale, int causal, int window_left,
+                        int window_right, void* stream);
+
+int attn_fwd_varlen_persistent(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                               int total_tokens, int heads_q, int heads_kv, int head_dim,
+                               int dtype, float softmax_scale, int causal, int window_left,
+                               int window_right, void* stream);
+
+/*
  * Split-KV variants, for problems whose plain grid cannot fill the GPU (few heads and q-tiles
  * over long sequences).  The key tiles that every q-tile sees are shared out among num_splits
  * work items; each writes a normalised fp32 partial output O_s and the natural-log LSE_s of

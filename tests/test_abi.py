@@ -347,3 +347,35 @@ def test_fp8_empty_problem_is_a_no_op(lib):
 
 def test_device_info_rejects_null_pointers(lib):
     assert lib.attn_device_info(0, None, None) == 1
+
+
+def call_persistent(lib, q=A, k=A, v=A, o=A, lse=None, b=1, h=2, hkv=1, n=16, d=128, dtype=1,
+                    scale=SCALE, causal=0, wl=-1, wr=-1):
+    return lib.attn_fwd_persistent(q, k, v, o, lse, b, h, hkv, n, d, dtype, scale, causal, wl,
+                                   wr, None)
+
+
+def call_varlen_persistent(lib, cu=A, ns=2, maxs=8, total=16, h=2, hkv=1, d=128, **kw):
+    q, k, v, o = (kw.pop(x, A) for x in "qkvo")
+    return lib.attn_fwd_varlen_persistent(q, k, v, o, None, cu, ns, maxs, total, h, hkv, d, 1,
+                                          SCALE, 0, -1, -1, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), 2), (dict(d=256), 2), (dict(d=96), 2), (dict(hkv=3), 1), (dict(hkv=0), 1),
+    (dict(q=None), 1), (dict(dtype=5), 3), (dict(k=A + 8), 4), (dict(scale=0.0), 1),
+    (dict(causal=3), 1), (dict(n=1 << 23), 5),
+])
+def test_persistent_rejects_bad_arguments(lib, kw, status):
+    assert call_persistent(lib, **kw) == status
+
+
+def test_persistent_empty_problem_is_a_no_op(lib):
+    assert call_persistent(lib, q=None, k=None, v=None, o=None, n=0) == 0
+    assert call_varlen_persistent(lib, q=None, k=None, v=None, o=None, cu=None, ns=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [(dict(d=64), 2), (dict(cu=None), 1), (dict(maxs=17), 1),
+                                       (dict(hkv=3), 1)])
+def test_varlen_persistent_rejects_bad_arguments(lib, kw, status):
+    assert call_varlen_persistent(lib, **kw) == status

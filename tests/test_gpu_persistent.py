@@ -1,8 +1,9 @@
-"""GPU parity of the persistent ping-pong kernel (head dim 128, big grids): one workgroup per
-compute unit sweeps a list of q-tiles as one pipeline.  The cases stress the list: many q-tiles
+"""GPU parity of the persistent ping-pong kernel (attn_fwd_persistent, attn_fwd_varlen_persistent;
+head dim 128): one workgroup per compute unit sweeps a list of q-tiles as one pipeline.  The cases stress the list: many q-tiles
 per workgroup, packed batches whose q-tiles have a single key tile (the tile loads then look
 further down the list), empty and one-token sequences (slots with nothing to compute), masks,
-and grouped K/V heads.  Every compared head is compared in full with the fp64 oracle."""
+and grouped K/V heads.  Every compared head is compared in full with the fp64 oracle.  The
+grouped-head packing of the default grid-launched ping-pong kernel is checked here too."""
 
 import math
 
@@ -10,8 +11,9 @@ import pytest
 import torch
 
 import bench
-from exact_attention_49_amd import attn_fwd_varlen_gqa, inputs
-from tests.gpu_helpers import check_all_heads_dense, check_all_heads_varlen, gpu_dense
+from exact_attention_49_amd import (AttnError, attn_fwd, attn_fwd_gqa, attn_fwd_persistent,
+                                    attn_fwd_varlen_persistent, inputs)
+from tests.gpu_helpers import check_all_heads_dense, check_all_heads_varlen
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -29,11 +31,9 @@ def test_persistent_packed_short_sequences(causal, wl, wr, hkv):
     heads = 96   # 96 heads x 12 q-tiles of 256 rows: 1152 slots, about 4.5 per workgroup
     q, k, v, cu = inputs.make_varlen(len(SHORT_MIX), 0, 0, heads, 128, "bf16", seed=1500 + hkv,
                                      lengths=SHORT_MIX, heads_kv=hkv)
-    w = inputs.Workload(name="t", heads=heads, head_dim=128, dtype="bf16", causal=causal,
-                        seed=0, num_seqs=len(SHORT_MIX), window_left=wl, window_right=wr)
-    assert bench.kernel_name(w, cu) == "attn_fwd_pp_kernel"
-    o, lse = attn_fwd_varlen_gqa(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(SHORT_MIX),
-                                 causal=causal, window_left=wl, window_right=wr)
+    o, lse = attn_fwd_varlen_persistent(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV),
+                                        max(SHORT_MIX), causal=causal, window_left=wl,
+                                        window_right=wr)
     torch.cuda.synchronize()
     check_all_heads_varlen(q, k, v, cu, o, lse, 1 / math.sqrt(128), causal, wl, wr,
                            torch.bfloat16, "persistent packed")
@@ -49,7 +49,8 @@ def test_persistent_dense_many_items(shape, causal, dt):
     b, h, n = shape
     print(f"[case] persistent dense B{b} H{h} N{n} causal={causal} {dt}", flush=True)
     q, k, v = inputs.make_dense(b, h, n, 128, dt, seed=1600 + h)
-    o, lse = gpu_dense(q, k, v, causal)
+    o, lse = attn_fwd_persistent(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
     sel = sorted({0, h // 2, h - 1})
     for hd in sel:
         sl = slice(hd, hd + 1)
@@ -57,7 +58,7 @@ def test_persistent_dense_many_items(shape, causal, dt):
                               1 / math.sqrt(128), causal, -1, -1, DTYPES[dt], f"head {hd}")
 
 
-# (B, Hq, Hkv, N): grouped K/V heads on the persistent kernel; the query heads of a K/V head
+# (B, Hq, Hkv, N): grouped K/V heads on the ping-pong kernels; the query heads of a K/V head
 # are packed into one q-tile by the largest power of two dividing the group, at most 8:
 # MQA (group 32: 8 heads of 32 positions per q-tile), group 3 (no packing), group 6 (2 heads
 # of 128 positions), group 12 (4 heads of 64 positions, ragged N)
@@ -72,7 +73,6 @@ def test_packed_heads_match_repeated_kv_and_oracle(shape, mask):
     """A packed q-tile computes each of its heads' rows with the same key tiles, in the same
     order, as an unpacked one: the grouped call must equal attn_fwd on K/V repeated along the
     heads bit for bit, and match the oracle (first, middle and last query head in full)."""
-    from exact_attention_49_amd import attn_fwd, attn_fwd_gqa
     b, hq, hkv, n = shape
     causal, wl, wr = PACK_MASKS[mask]
     print(f"[case] packed heads {shape} {mask}", flush=True)
@@ -94,3 +94,29 @@ def test_packed_heads_match_repeated_kv_and_oracle(shape, mask):
         kh = slice(hd // g, hd // g + 1)
         check_all_heads_dense(q[:, sl], k[:, kh], v[:, kh], o[:, sl], lse[:, sl],
                               1 / math.sqrt(128), causal, wl, wr, torch.bfloat16, f"head {hd}")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "causal_w200"])
+@pytest.mark.parametrize("shape", PACKED)
+def test_persistent_packed_heads_match_oracle(shape, mask):
+    """The persistent kernel on grouped K/V heads (packed q-tiles): first, middle and last
+    query head in full against the oracle."""
+    b, hq, hkv, n = shape
+    causal, wl, wr = PACK_MASKS[mask]
+    print(f"[case] persistent packed heads {shape} {mask}", flush=True)
+    q, k, v = inputs.make_dense(b, hq, n, 128, "bf16", seed=1800 + hq + hkv, heads_kv=hkv)
+    o, lse = attn_fwd_persistent(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal,
+                                 window_left=wl, window_right=wr)
+    torch.cuda.synchronize()
+    g = hq // hkv
+    for hd in sorted({0, hq // 2, hq - 1}):
+        sl = slice(hd, hd + 1)
+        kh = slice(hd // g, hd // g + 1)
+        check_all_heads_dense(q[:, sl], k[:, kh], v[:, kh], o[:, sl], lse[:, sl],
+                              1 / math.sqrt(128), causal, wl, wr, torch.bfloat16, f"head {hd}")
+
+
+def test_persistent_rejects_other_head_dims():
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(AttnError, match="UNSUPPORTED_HEAD_DIM"):
+        attn_fwd_persistent(q, q, q)
