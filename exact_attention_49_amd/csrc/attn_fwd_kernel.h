@@ -227,10 +227,15 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 
   if (!wave_active) return;
-  if constexpr (SPLIT)
+  if constexpr (SPLIT) {
     store_rows_partial<D>(a, w.split, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
-  else
-    store_rows<BF16, D>(a, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
+  } else {
+    // every wave is past the sweep's last barrier and no tile load is in flight: the tile
+    // buffers are free, 32 rows of 2D bytes per wave
+    static_assert(BR * ROWB <= STAGES * 2 * TILEB, "the output rows fit the tile buffers");
+    store_rows_staged<BF16, D>(a, w.row0, qrow, seqlen, oacc, m_run, l_run,
+                               smem + __builtin_amdgcn_readfirstlane(wave) * 32 * ROWB);
+  }
 }
 
 }  // namespace xattn

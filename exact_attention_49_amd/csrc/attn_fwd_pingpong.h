@@ -301,10 +301,20 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       if (j + 1 <= n) iteration(j + 1, std::integral_constant<int, 1>{});
     }
 
-    if (wave_active) store_rows<BF16, D>(a, wrow0, qrow, seqlen, hh, oacc, m_run, l_run);
+    // all waves are past the sweep's last barrier and no tile load is in flight: the four
+    // tile buffers are free, 8 KiB (32 rows of 2D bytes at d = 128) per wave
+    static_assert(8 * 32 * D * 2 <= 4 * TILEB, "the output rows fit the tile buffers");
+    char* const region = (wave >> 1) == 0   ? k_lds0
+                         : (wave >> 1) == 1 ? k_lds1
+                         : (wave >> 1) == 2 ? v_lds0
+                                            : v_lds1;
+    if (wave_active)
+      store_rows_staged<BF16, D>(a, wrow0, qrow, seqlen, oacc, m_run, l_run,
+                                 region + (wave & 1) * (TILEB / 2));
   };
   run_tile(w0);
-  if (light >= 0) {  // the pair's second tile: the LDS buffers are free after the last barrier
+  if (light >= 0) {  // the pair's second tile, once every wave has read its staged rows back
+    block_barrier();
     Work w1 = w0;
     w1.tile = light;
     run_tile(w1);

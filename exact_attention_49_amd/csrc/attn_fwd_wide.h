@@ -89,44 +89,6 @@ __device__ __forceinline__ void mma_pv_agpr(const char* vt, const LaneOffsets<D>
   }
 }
 
-// Epilogue of one wave's 32 rows: O / l rounded to 16-bit, staged in this wave's LDS region
-// (32 rows x 2D bytes, 16-byte chunk c of row r at chunk position c ^ r) and read back row by
-// row, so that every global store instruction writes whole rows.  Rows past the end of the
-// sequence are not stored.  LSE = (m + log2 l) ln 2.  Called by all lanes of the wave; the
-// region must not be in use by any other wave.
-template <bool BF16, int D>
-__device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, int qw0, int seqlen,
-                                                  int lane, const f32x16 (&o)[D / 32],
-                                                  float m_run, float l_run, char* region) {
-  constexpr float LN2 = 0.693147180559945309f;
-  constexpr int ROWB = D * 2, CH = D / 8, RPI = 64 / CH;  // rows per 64-lane read
-  static_assert(CH <= 64 && 64 % CH == 0 && CH >= 32, "one row spans 32 or 64 chunks");
-  const int l32 = lane & 31, hh = lane >> 5;
-  const float lt = halves_sum(l_run);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x16& x = o[db];
-      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
-                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
-      const int c = 4 * db + g4;  // 16-byte chunk of d = 32 db + 8 g4 .. + 7; this lane's half hh
-      *(i32x2*)(region + l32 * ROWB + ((c ^ l32) << 4) + hh * 8) = val;
-    }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  const int rsub = lane / CH, c = lane % CH;
-#pragma unroll
-  for (int r0 = 0; r0 < 32; r0 += RPI) {
-    const int r = r0 + rsub;
-    const i32x4 v = *(const i32x4*)(region + r * ROWB + ((c ^ r) << 4));
-    if (qw0 + r < seqlen) *(i32x4*)(a.o + (row0 + qw0 + r) * D + c * 8) = v;
-  }
-  const int qrow = qw0 + l32;
-  if (a.lse != nullptr && hh == 0 && qrow < seqlen)
-    a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
-}
-
 // SPLIT: split-KV mode (the workgroup sweeps its split's share of the key tiles and writes
 // fp32 partial results; see FwdArgs).
 template <bool BF16, int D, int MODE, bool SPLIT = false>
@@ -312,7 +274,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   if constexpr (SPLIT)
     store_rows_partial<D>(a, w.split, w.row0, qrow, seqlen, hh, oacc, m_run, l_run);
   else
-    store_rows_staged<BF16, D>(a, w.row0, qw0, seqlen, lane, oacc, m_run, l_run, region);
+    store_rows_staged<BF16, D>(a, w.row0, qrow, seqlen, oacc, m_run, l_run, region);
 }
 
 }  // namespace xattn
