@@ -76,22 +76,6 @@ __device__ __forceinline__ float dot8(i32x4 x, i32x4 y) {
   return acc;
 }
 
-// Stores the lane's row of a transposed accumulator (register r of column block db holds
-// d = 32 db + 8 (r / 4) + 4 hh + r % 4), multiplied by `mul` and rounded to 16 bits.
-template <bool BF16, int D>
-__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[D / 32], float mul,
-                                          int hh) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x16& x = acc[db];
-      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * mul, x[4 * g4 + 1] * mul),
-                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * mul, x[4 * g4 + 3] * mul)};
-      *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
-    }
-}
-
 // Packs score-layout fp32 values (two 32-row blocks of 16 registers per 64) to the 16-bit
 // B operand of a transposed-accumulator product, as the forward packs P.
 template <bool BF16, int BN>
@@ -262,7 +246,14 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     block_barrier();
   }
 
-  if (wave_active && qrow < seqlen) store_row<BF16, D>(ba.dq + grow * D, dqacc, ba.scale, hh);
+  // every wave is past the sweep's last barrier and no tile load is in flight: the tile
+  // buffers hold each wave's 32 rows of dQ for whole-row stores
+  static_assert(BR * ROWB <= 2 * STAGEB, "the dQ rows fit the tile buffers");
+  if (wave_active) {
+    const int row_w = qrow - l32;  // the wave's first row
+    store_block_staged<BF16, D>(ba.dq + (w.row0 + row_w) * D, seqlen - row_w, dqacc, ba.scale,
+                                smem + __builtin_amdgcn_readfirstlane(wave) * 32 * ROWB);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -544,11 +535,20 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   }
   if (dk_wave && tile_active(tile_base(n_it - 1))) consume_dk((n_it - 1) % 3);
 
-  if (wave_active && krow < seqlen) {
+  // Past the sweep's last barrier no load is in flight and only the dK waves' last step reads
+  // an LDS stage, (n_it - 1) % 3: the other two stages hold each wave's 32 rows of dK or dV
+  // (dV waves in one, dK waves in the other) for whole-row stores, with no further barrier.
+  static_assert((BwdShape::NW / 2) * 32 * ROWB <= STAGEB, "half the waves' rows fit a stage");
+  if (wave_active) {
+    const int row_w = krow - l32;  // the wave's first key row
+    const int stage = (n_it + (dk_wave ? 1 : 0)) % NSTAGE;
+    char* const region = smem + stage * STAGEB + __builtin_amdgcn_readfirstlane(pair) * 32 * ROWB;
     if (dk_wave)
-      store_row<BF16, D>(ba.dk + (w.kv_row0 + krow) * D, acc, ba.scale, hh);
+      store_block_staged<BF16, D>(ba.dk + (w.kv_row0 + row_w) * D, seqlen - row_w, acc,
+                                  ba.scale, region);
     else
-      store_row<BF16, D>(ba.dv + (w.kv_row0 + krow) * D, acc, 1.0f, hh);
+      store_block_staged<BF16, D>(ba.dv + (w.kv_row0 + row_w) * D, seqlen - row_w, acc, 1.0f,
+                                  region);
   }
 }
 

@@ -744,15 +744,15 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, long row0, int qrow
     a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
-// Epilogue of one wave's 32 rows through LDS, so that every global store writes whole rows
-// with 16-byte accesses: O / l rounded to 16-bit goes to the wave's region (32 rows x 2D
-// bytes), and is read back row by row.  In the region, the 8-byte half hh of 16-byte chunk c of
-// row r sits at chunk position c ^ g(r) and half position hh ^ bit 4 of r, with g(r) = r for
-// 32 or more chunks per row, r mod 16 for 16, and (r / 2) mod 8 for 8: each 32-lane half of a
-// write instruction then covers 32 distinct 8-byte bank slots and each 16-lane quarter of a
-// read covers 16 distinct 16-byte ones.  Rows past the end of the sequence are not stored.
-// LSE = (m + log2 l) ln 2.  Called by all lanes of the wave; the region must not be in use by
-// any other wave.
+// One wave's 32 rows of a transposed accumulator (register r of column block db holds
+// d = 32 db + 8 (r / 4) + 4 hh + r % 4 of the lane's row), times the lane's `mul` and rounded
+// to 16 bits, written through the wave's LDS region (32 rows x 2D bytes) so that every global
+// store writes whole rows with 16-byte accesses: row r goes to dst + r D for r < nrows.  In
+// the region, the 8-byte half hh of 16-byte chunk c of row r sits at chunk position c ^ g(r)
+// and half position hh ^ bit 4 of r, with g(r) = r for 32 or more chunks per row, r mod 16 for
+// 16, and (r / 2) mod 8 for 8: each 32-lane half of a write instruction then covers 32
+// distinct 8-byte bank slots and each 16-lane quarter of a read covers 16 distinct 16-byte
+// ones.  Called by all lanes of the wave; the region must not be in use by any other wave.
 template <int CH>
 __device__ __forceinline__ int staged_chunk(int c, int r) {
   if constexpr (CH == 8) return c ^ ((r >> 1) & 7);
@@ -760,26 +760,22 @@ __device__ __forceinline__ int staged_chunk(int c, int r) {
   else return c ^ r;
 }
 template <bool BF16, int D>
-__device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, int qrow, int seqlen,
-                                                  const f32x16 (&o)[D / 32], float m_run,
-                                                  float l_run, char* region) {
-  constexpr float LN2 = 0.693147180559945309f;
+__device__ __forceinline__ void store_block_staged(uint16_t* dst, int nrows,
+                                                   const f32x16 (&acc)[D / 32], float mul,
+                                                   char* region) {
   constexpr int ROWB = D * 2, CH = D / 8, RPI = 64 / CH;  // rows per 64-lane read
   static_assert(CH >= 8 && CH <= 64 && 64 % CH == 0, "one row spans 8 to 64 chunks");
-  // the lane index, recomputed here rather than kept live through the sweep
+  // the lane index, recomputed here rather than kept live through a kernel's main loop
   const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qw0 = qrow - l32;  // the wave's first row
-  const float lt = halves_sum(l_run);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   char* const wrow = region + l32 * ROWB + ((hh ^ ((l32 >> 4) & 1)) << 3);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x16& x = o[db];
-      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
-                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
+      const f32x16& x = acc[db];
+      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * mul, x[4 * g4 + 1] * mul),
+                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * mul, x[4 * g4 + 3] * mul)};
       const int c = 4 * db + g4;  // 16-byte chunk of d = 32 db + 8 g4 .. + 7; this lane's half hh
       *(i32x2*)(wrow + (staged_chunk<CH>(c, l32) << 4)) = val;
     }
@@ -790,9 +786,23 @@ __device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, i
     const int r = r0 + rsub;
     i32x4 v = *(const i32x4*)(region + r * ROWB + (staged_chunk<CH>(c, r) << 4));
     if ((r0 >> 4) & 1) v = (i32x4){v[2], v[3], v[0], v[1]};  // halves stored swapped
-    if (qw0 + r < seqlen) *(i32x4*)(a.o + (row0 + qw0 + r) * D + c * 8) = v;
+    if (r < nrows) *(i32x4*)(dst + (long)r * D + c * 8) = v;
   }
-  if (a.lse != nullptr && hh == 0 && qrow < seqlen)
+}
+
+// Epilogue for one wave's 32 rows: O = O / l through store_block_staged and
+// LSE = (m + log2 l) ln 2.  Rows past the end of the sequence are not stored.  Called by all
+// lanes of the wave; the region must not be in use by any other wave.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, int qrow, int seqlen,
+                                                  const f32x16 (&o)[D / 32], float m_run,
+                                                  float l_run, char* region) {
+  constexpr float LN2 = 0.693147180559945309f;
+  const float lt = halves_sum(l_run);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int qw0 = qrow - (__lane_id() & 31);  // the wave's first row
+  store_block_staged<BF16, D>(a.o + (row0 + qw0) * D, seqlen - qw0, o, inv, region);
+  if (a.lse != nullptr && (__lane_id() >> 5) == 0 && qrow < seqlen)
     a.lse[row0 + qrow] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 

@@ -325,19 +325,26 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   // epilogue: O = O * descale_v / l, LSE = (m - 8 + log2 l) ln 2
   constexpr float LN2 = 0.693147180559945309f;
   const float lt = halves_sum(l_run);
-  if (qrow >= seqlen) return;
   const float inv = lt > 0.f ? dsv / lt : 0.f;
-  uint16_t* dst = a.o + (w.row0 + qrow) * D;
+  if constexpr ((BR / 32) * 32 * D * 2 <= (int)sizeof(smem)) {
+    // every wave is past the sweep's last barrier and no tile load is in flight: the tile
+    // buffers hold each wave's 32 rows of 16-bit output for whole-row stores
+    const int row_w = qrow - (__lane_id() & 31);  // the wave's first row
+    store_block_staged<BF16, D>(a.o + (w.row0 + row_w) * D, seqlen - row_w, oacc, inv,
+                                smem + __builtin_amdgcn_readfirstlane(wave) * 32 * D * 2);
+  } else if (qrow < seqlen) {
+    uint16_t* dst = a.o + (w.row0 + qrow) * D;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x16& x = oacc[db];
-      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
-                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
-      *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
-    }
-  if (a.lse != nullptr && hh == 0)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& x = oacc[db];
+        const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * inv, x[4 * g4 + 1] * inv),
+                           (int)Elt<BF16>::pack2(x[4 * g4 + 2] * inv, x[4 * g4 + 3] * inv)};
+        *(i32x2*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
+      }
+  }
+  if (a.lse != nullptr && hh == 0 && qrow < seqlen)
     a.lse[w.row0 + qrow] = lt > 0.f ? (m_run - OFFSET + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
