@@ -747,15 +747,20 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, long row0, int qrow
 // One wave's 32 rows of a transposed accumulator (register r of column block db holds
 // d = 32 db + 8 (r / 4) + 4 hh + r % 4 of the lane's row), times the lane's `mul` and rounded
 // to 16 bits, written through the wave's LDS region (32 rows x 2D bytes) so that every global
-// store writes whole rows with 16-byte accesses: row r goes to dst + r D for r < nrows.  In
-// the region, the 8-byte half hh of 16-byte chunk c of row r sits at chunk position c ^ g(r)
-// and half position hh ^ bit 4 of r, with g(r) = r for 32 or more chunks per row, r mod 16 for
-// 16, and (r / 2) mod 8 for 8: each 32-lane half of a write instruction then covers 32
-// distinct 8-byte bank slots and each 16-lane quarter of a read covers 16 distinct 16-byte
-// ones.  Called by all lanes of the wave; the region must not be in use by any other wave.
+// store writes whole rows with 16-byte accesses: row r goes to dst + r D for r < nrows.
+// The two 8-byte halves of a 16-byte chunk of a row sit in lanes l and l + 32; one
+// v_permlane32_swap per dword gathers chunk 4 db + 2 gp in the low lane and chunk
+// 4 db + 2 gp + 1 in the high one, so each lane writes whole chunks (ds_write_b128).  Chunk c
+// of row r sits at chunk position c ^ g(r), with g(r) = r for 32 or more chunks per row,
+// r mod 16 for 16 and r mod 8 for 8, so that any 8 consecutive rows put one chunk into 8
+// different 16-byte slots of a 128-byte bank window: the SQ_LDS_BANK_CONFLICT counter shows a
+// 16-byte write served 8 lanes at a time over 128 bytes (at 8 chunks per row, the K tile's
+// two-rows-per-window swizzle costs 2-way conflicts here), and the read-back, a whole row per
+// 8 or 16 lanes, is free of conflicts for any g.  Called by all lanes of the wave; the region
+// must not be in use by any other wave.
 template <int CH>
 __device__ __forceinline__ int staged_chunk(int c, int r) {
-  if constexpr (CH == 8) return c ^ ((r >> 1) & 7);
+  if constexpr (CH == 8) return c ^ (r & 7);
   else if constexpr (CH == 16) return c ^ (r & 15);
   else return c ^ r;
 }
@@ -768,24 +773,30 @@ __device__ __forceinline__ void store_block_staged(uint16_t* dst, int nrows,
   // the lane index, recomputed here rather than kept live through a kernel's main loop
   const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int l32 = lane & 31, hh = lane >> 5;
-  char* const wrow = region + l32 * ROWB + ((hh ^ ((l32 >> 4) & 1)) << 3);
+  char* const wrow = region + l32 * ROWB;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
+    for (int gp = 0; gp < 2; ++gp) {
       const f32x16& x = acc[db];
-      const i32x2 val = {(int)Elt<BF16>::pack2(x[4 * g4 + 0] * mul, x[4 * g4 + 1] * mul),
-                         (int)Elt<BF16>::pack2(x[4 * g4 + 2] * mul, x[4 * g4 + 3] * mul)};
-      const int c = 4 * db + g4;  // 16-byte chunk of d = 32 db + 8 g4 .. + 7; this lane's half hh
-      *(i32x2*)(wrow + (staged_chunk<CH>(c, l32) << 4)) = val;
+      const int r0 = 8 * gp;  // registers r0..r0+3: 4 columns of chunk 4 db + 2 gp; r0+4..: of the next
+      const uint32_t x0 = Elt<BF16>::pack2(x[r0 + 0] * mul, x[r0 + 1] * mul);
+      const uint32_t x1 = Elt<BF16>::pack2(x[r0 + 2] * mul, x[r0 + 3] * mul);
+      const uint32_t y0 = Elt<BF16>::pack2(x[r0 + 4] * mul, x[r0 + 5] * mul);
+      const uint32_t y1 = Elt<BF16>::pack2(x[r0 + 6] * mul, x[r0 + 7] * mul);
+      // low lanes keep x and take the high lanes' x; high lanes take the low lanes' y
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      const i32x4 val = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      const int c = 4 * db + 2 * gp + hh;
+      *(i32x4*)(wrow + (staged_chunk<CH>(c, l32) << 4)) = val;
     }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   const int rsub = lane / CH, c = lane % CH;
 #pragma unroll
   for (int r0 = 0; r0 < 32; r0 += RPI) {
     const int r = r0 + rsub;
-    i32x4 v = *(const i32x4*)(region + r * ROWB + (staged_chunk<CH>(c, r) << 4));
-    if ((r0 >> 4) & 1) v = (i32x4){v[2], v[3], v[0], v[1]};  // halves stored swapped
+    const i32x4 v = *(const i32x4*)(region + r * ROWB + (staged_chunk<CH>(c, r) << 4));
     if (r < nrows) *(i32x4*)(dst + (long)r * D + c * 8) = v;
   }
 }
