@@ -12,8 +12,10 @@ One step = one forward pass (one attn_fwd / attn_fwd_varlen call, attn_fwd_gqa f
 grouped-query workload; for the split-KV workload one attn_fwd_splitkv call, which runs the
 split sweep and the merge; for the backward workload one attn_bwd call, its two kernels, with
 the forward's O and LSE computed before timing) over the workload's
-inputs, which are resident in HBM before timing starts.  W untimed steps, then exactly K timed
-steps between two device synchronisations.  Rank 0 prints one JSON line:
+inputs, which are resident in HBM before timing starts.  The step first repeats untimed for
+0.3 s while the engine clock ramps up under load (config.clock_settle records how many), then
+W untimed warm-up steps, then exactly K timed steps between two device synchronisations.
+Rank 0 prints one JSON line:
 
   value    whole-job TFLOP/s with F = 4*B*H*N^2*d, halved when causal (packed batches count
            the visible (query, key) pairs: F = 4*H*d*sum_s pairs_s)
@@ -337,7 +339,7 @@ FIVE_CONFIGS = ("tiny_fp16_d64", "causal_bf16_d128_n2048", "causal_bf16_d128_n81
 
 
 def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = True,
-                 cpu_budget: float | None = 20.0) -> dict:
+                 cpu_budget: float | None = 20.0, settle_s: float = 0.3) -> dict:
     """Time `steps` steps of one workload after `warmup` untimed ones and return its record:
     whole-job throughput, the dominant kernel's roofline from HIP-event launch durations,
     counter figures from profiles/ (when taken on the current sources), and, unless
@@ -403,6 +405,16 @@ def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = T
                 qd, kd, vd, causal=w.causal, window_left=w.window_left,
                 window_right=w.window_right, out=od, lse=lsed)
 
+    # The engine clock ramps up over the first 0.1-0.2 s of sustained load: repeat the step for
+    # settle_s seconds first, so that the warm-up and the timed steps run at the steady clock.
+    settle_steps = 0
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter() + settle_s
+    while time.perf_counter() < t_settle:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 4
     for _ in range(warmup):
         if flush_buf is not None:
             flush_buf.fill_(1)
@@ -461,6 +473,8 @@ def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = T
               "head_dim": w.head_dim, "dtype": w.dtype,
               "causal": w.causal, "window_left": w.window_left,
               "window_right": w.window_right, "seed": w.seed, "value_scale": w.value_scale}
+    # untimed launches before the warm-up steps while the engine clock settles
+    config["clock_settle"] = {"seconds": settle_s, "steps": settle_steps}
     if w.varlen:
         lens = (cu[1:] - cu[:-1]).tolist()
         config.update(num_seqs=w.num_seqs, total_tokens=int(cu[-1]), lengths=lens,
