@@ -120,3 +120,61 @@ def test_persistent_rejects_other_head_dims():
     q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(AttnError, match="UNSUPPORTED_HEAD_DIM"):
         attn_fwd_persistent(q, q, q)
+
+
+@pytest.mark.parametrize("mask", ["causal", "none", "causal_w200"])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (24, 2)])
+def test_packed_heads_varlen_default_path(hq, hkv, mask):
+    """Packed query heads on a packed batch through the default entry point (grid-launched
+    ping-pong kernel): bitwise equal to attn_fwd_varlen on repeated K/V, and three query heads
+    in full against the oracle.  Lengths include empty, one-token and ragged sequences."""
+    from exact_attention_49_amd import attn_fwd_varlen, attn_fwd_varlen_gqa
+    causal, wl, wr = PACK_MASKS[mask]
+    lens = [700, 0, 1, 513, 1290, 64, 257, 900, 3, 400]
+    print(f"[case] packed heads varlen default Hq{hq} Hkv{hkv} {mask}", flush=True)
+    q, k, v, cu = inputs.make_varlen(len(lens), 0, 0, hq, 128, "bf16", seed=1900 + hq + hkv,
+                                     lengths=lens, heads_kv=hkv)
+    w = inputs.Workload(name="t", heads=hq, heads_kv=hkv, head_dim=128, dtype="bf16",
+                        causal=causal, seed=0, num_seqs=len(lens), window_left=wl,
+                        window_right=wr)
+    assert bench.kernel_name(w, cu) == "attn_fwd_pp_kernel"
+    o, lse = attn_fwd_varlen_gqa(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lens),
+                                 causal=causal, window_left=wl, window_right=wr)
+    g = hq // hkv
+    o2, lse2 = attn_fwd_varlen(q.to(DEV), k.repeat_interleave(g, 0).to(DEV),
+                               v.repeat_interleave(g, 0).to(DEV), cu.to(DEV), max(lens),
+                               causal=causal, window_left=wl, window_right=wr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for hd in sorted({0, hq // 2, hq - 1}):
+        sl = slice(hd, hd + 1)
+        kh = slice(hd // g, hd // g + 1)
+        check_all_heads_varlen(q[sl], k[kh], v[kh], cu, o[sl], lse[sl], 1 / math.sqrt(128),
+                               causal, wl, wr, torch.bfloat16, f"head {hd}")
+
+
+@pytest.mark.parametrize("mask", ["causal", "window_30_70"])
+def test_packed_heads_fp16(mask):
+    """fp16 on the packed ping-pong kernel (group 8: 8 heads of 32 positions per q-tile)."""
+    from exact_attention_49_amd import attn_fwd, attn_fwd_gqa
+    b, hq, hkv, n = 2, 32, 4, 2100
+    causal, wl, wr = PACK_MASKS[mask]
+    print(f"[case] packed heads fp16 {mask}", flush=True)
+    q, k, v = inputs.make_dense(b, hq, n, 128, "fp16", seed=1950, heads_kv=hkv)
+    w = inputs.Workload(name="t", heads=hq, heads_kv=hkv, head_dim=128, dtype="fp16",
+                        causal=causal, seed=0, batch=b, seqlen=n, window_left=wl,
+                        window_right=wr)
+    assert bench.kernel_name(w) == "attn_fwd_pp_kernel"
+    o, lse = attn_fwd_gqa(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window_left=wl,
+                          window_right=wr)
+    g = hq // hkv
+    o2, lse2 = attn_fwd(q.to(DEV), k.repeat_interleave(g, 1).to(DEV),
+                        v.repeat_interleave(g, 1).to(DEV), causal=causal, window_left=wl,
+                        window_right=wr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    for hd in (0, hq - 1):
+        sl = slice(hd, hd + 1)
+        kh = slice(hd // g, hd // g + 1)
+        check_all_heads_dense(q[:, sl], k[:, kh], v[:, kh], o[:, sl], lse[:, sl],
+                              1 / math.sqrt(128), causal, wl, wr, torch.float16, f"head {hd}")
