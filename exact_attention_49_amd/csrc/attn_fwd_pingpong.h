@@ -36,6 +36,10 @@
 // positions of each, wave w computing 32 positions of head w / (8 / pack), so that all eight
 // waves use every K/V tile the workgroup loads.  The work decoding treats each packed group of
 // query heads as one head of BR / pack rows per q-tile.
+//
+// After a q-tile's last barrier the four tile buffers are free: each wave stages its 32 output
+// rows in 8 KiB of them and stores whole rows (store_rows_staged); a folded pair's second
+// tile starts with one more barrier, once every wave has read its rows back.
 #pragma once
 
 #include <type_traits>
