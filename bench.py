@@ -81,14 +81,23 @@ def kernel_family(w, cu=None) -> str:
     return "pingpong" if name == "attn_fwd_pp_kernel" else "generic"
 
 
+def _code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed (string literals in
+    these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(family: str) -> str:
-    """Hash of the HIP sources of one kernel family (KERNEL_SOURCES): recorded HBM counters
-    are only valid for the kernels they were taken on."""
+    """Hash of the code (comments and layout excluded) of the HIP sources of one kernel family
+    (KERNEL_SOURCES): recorded HBM counters are only valid for the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_49_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
