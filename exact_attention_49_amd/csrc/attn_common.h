@@ -474,14 +474,21 @@ __device__ __forceinline__ void load_q_nowait(const uint16_t* qp, int row, int s
   for (int c = 0; c < D / 16; ++c)
     qf[c] = (row < seqlen) ? src[2 * c + hh] : (i32x4){0, 0, 0, 0};
 }
+// q_arrived marks the fragments as used here, so that the compiler places the wait for their
+// loads at this point and not at their first use inside the K/V sweep (where it would also
+// wait for tile loads still in flight: the compiler does not see the loads into LDS).  Kernels
+// issue their Q loads, then their first tile loads, then call it, so that the two latencies
+// overlap.
+template <int D>
+__device__ __forceinline__ void q_arrived(const i32x4 (&qf)[D / 16]) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
+}
 template <int D>
 __device__ __forceinline__ void load_q(const uint16_t* qp, int row, int seqlen, int hh,
                                        i32x4 (&qf)[D / 16]) {
   load_q_nowait<D>(qp, row, seqlen, hh, qf);
-  // Consume the fragments here, so the wait for these loads sits before the K/V sweep instead
-  // of inside it (where it would also wait for tile loads still in flight).
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
+  q_arrived<D>(qf);
 }
 
 // Per-lane LDS byte offsets of the MFMA operand reads.  The swizzle key of every row a lane

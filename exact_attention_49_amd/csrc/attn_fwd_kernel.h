@@ -72,7 +72,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const int qrow = qw0 + l32;
 
   i32x4 qf[D / 16];
-  load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
+  load_q_nowait<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);  // waited for after the first tile loads
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
 
   f32x16 oacc[D / 32];
@@ -191,6 +191,7 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr int LEAD = STAGES - 1;
     if (n_tiles > 0) dma_tile(t_lo, 0);
     if (LEAD == 2 && n_tiles > 1) dma_tile(t_lo + 1, 1);
+    q_arrived<D>(qf);
     wait_older(LEAD == 2 && n_tiles > 1);
     block_barrier();
     int s = 0;
@@ -204,10 +205,9 @@ void attn_fwd_kernel(FwdArgs a) {
       s = s + 1 < STAGES ? s + 1 : 0;
     }
   } else if constexpr (STAGES == 2) {
-    if (n_tiles > 0) {
-      gload(t_lo);
-      lstore(0);
-    }
+    if (n_tiles > 0) gload(t_lo);
+    q_arrived<D>(qf);
+    if (n_tiles > 0) lstore(0);
     __syncthreads();
     for (int t = t_lo; t <= t_hi; ++t) {
       const int s = (t - t_lo) & 1;
@@ -217,6 +217,7 @@ void attn_fwd_kernel(FwdArgs a) {
       __syncthreads();
     }
   } else {
+    q_arrived<D>(qf);
     for (int t = t_lo; t <= t_hi; ++t) {
       if (t > t_lo) __syncthreads();
       gload(t);

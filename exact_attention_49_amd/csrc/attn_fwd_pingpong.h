@@ -142,7 +142,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
     const int qrow = qw0 + l32;
 
     i32x4 qf[D / 16];
-    load_q<D>(a.q + wrow0 * D, qrow, seqlen, hh, qf);
+    load_q_nowait<D>(a.q + wrow0 * D, qrow, seqlen, hh, qf);  // waited for after the prologue loads
     const LaneOffsets<D> lo = lane_offsets<D>(lane);
 
     f32x16 oacc[D / 32];
@@ -262,8 +262,9 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       load_all(K_TILE, 0, k_lds1a);
       load_all(V_TILE, 0, v_lds0a);
       if (n > 1) load_all(K_TILE, 1, k_lds0a);
-      wait_vmem();
     }
+    q_arrived<D>(qf);
+    if (!grp_a) wait_vmem();
     block_barrier();
     if (grp_a) step_scores(0, k_lds1);
 

@@ -144,7 +144,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   const int qrow = qw0 + l32;
 
   i32x4 qf[D / 16];
-  load_q<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);
+  load_q_nowait<D>(a.q + w.row0 * D, qrow, seqlen, hh, qf);  // waited for after the first tile loads
   const LaneOffsets<D> lo = lane_offsets<D>(lane);
 
   f32x16 oacc[D / 32];
@@ -254,6 +254,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   const unsigned k0a = lds_address(k_lds0), k1a = lds_address(k_lds1);
   const unsigned v0a = lds_address(v_lds0), v1a = lds_address(v_lds1);
   if (n > 0) load_tile(t_lo, k0a, v0a);
+  q_arrived<D>(qf);
   wait_vmem();
   block_barrier();
   for (int t = t_lo; t <= t_hi; t += 2) {
