@@ -516,6 +516,11 @@ def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = T
                                            "GRBM_GUI_ACTIVE / 8 XCDs)")
     if "clock_mhz_measured" in counters:
         roof["clock_mhz_measured"] = counters["clock_mhz_measured"]
+    if "sq_valu_mfma_busy_cycles" in counters:
+        # the profile's MFMA-busy cycles per dispatch against this run's launch time at the
+        # nominal clock (equal to frac when the MFMA count is the algorithmic one)
+        roof["mfma_busy_frac_nominal"] = round(
+            counters["sq_valu_mfma_busy_cycles"] / 1024 / (avg_launch_s * 2.4e9), 4)
     out = {
         "metric": METRIC_BWD if w.backward else METRIC, "value": round(value, 2),
         "unit": "TFLOP/s", "n_gpus": 1,
@@ -570,7 +575,7 @@ def config_summary(rec: dict) -> dict:
            "algorithmic_bytes": roof["algorithmic_bytes"],
            "algorithmic_hbm_gbs": roof["algorithmic_hbm_gbs"]}
     for key in ("traffic", "traffic_over_algorithmic", "measured_hbm_gbs", "mfma_busy_frac",
-                "clock_mhz_measured"):
+                "mfma_busy_frac_nominal", "clock_mhz_measured"):
         if roof.get(key) is not None:
             row[key] = roof[key]
     cb = rec.get("cpu_baseline")
