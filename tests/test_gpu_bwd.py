@@ -205,25 +205,31 @@ def test_bwd_is_deterministic():
         assert torch.equal(x.cpu(), y.cpu())
 
 
-def test_bwd_full_length_head_of_benchmark_shape():
-    """B=2 H=32 N=8192 d=128 causal bf16 on the GPU; two (batch, head) pairs against the
-    oracle in full (with plain multi-head attention a head's gradients depend only on it)."""
+def test_bwd_full_length_heads_of_benchmark_shape():
+    """B=2 H=32 N=8192 d=128 causal bf16 on the GPU; every (batch, head) pair against the
+    oracle in full, element by element (with plain multi-head attention a head's gradients
+    depend only on it)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from tests.gpu_helpers import _oracle_workers
     w = inputs.WORKLOADS["causal_bf16_d128_n8192"]
     _announce("bwd " + w.name)
     q, k, v = inputs.make_workload(w)
     do = inputs.make_upstream(q.shape, w.dtype, seed=w.seed + 100, value_scale=w.value_scale)
     m = dict(causal=w.causal, wl=w.window_left, wr=w.window_right)
     dq, dk, dv = (g.cpu() for g in _gpu_dense(q, k, v, do, m))
-    for (b, h) in [(0, 0), (1, 31)]:
-        ref = oracle.attention_head_backward(q[b, h].double().numpy(), k[b, h].double().numpy(),
-                                             v[b, h].double().numpy(),
-                                             do[b, h].double().numpy(), w.softmax_scale,
-                                             w.causal, w.window_left, w.window_right)
-        scales = _head_scales(q[b, h].double().numpy(), k[b, h].double().numpy(),
-                              v[b, h].double().numpy(), do[b, h].double().numpy(),
-                              w.softmax_scale, w.causal, w.window_left, w.window_right)
-        _check((dq[b, h], dk[b, h], dv[b, h]), ref, torch.bfloat16, f"{w.name} ({b},{h})",
-               scales)
+
+    def one(bh):
+        b, h = bh
+        args = (q[b, h].double().numpy(), k[b, h].double().numpy(), v[b, h].double().numpy(),
+                do[b, h].double().numpy(), w.softmax_scale, w.causal, w.window_left,
+                w.window_right)
+        ref = oracle.attention_head_backward(*args)
+        return _check((dq[b, h], dk[b, h], dv[b, h]), ref, torch.bfloat16,
+                      f"{w.name} ({b},{h})", _head_scales(*args))
+
+    pairs = [(b, h) for b in range(2) for h in range(32)]
+    with ThreadPoolExecutor(min(4, _oracle_workers())) as ex:
+        list(ex.map(one, pairs))
 
 
 def test_bwd_binding_errors():
