@@ -376,7 +376,8 @@ def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = T
 
     ws = None
     if w.splitkv:  # caller-owned workspace, allocated before any timing
-        nbytes = splitkv_workspace_size(w.batch, w.heads, w.seqlen, w.head_dim, 0)
+        nbytes = splitkv_workspace_size(w.batch, w.heads, w.seqlen, w.head_dim, 0, w.causal,
+                                        w.window_left)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     if w.fp8:  # E4M3 inputs with per-tensor descales, quantised before timing
         (q8, dsq), (k8, dsk), (v8, dsv) = (inputs.quantize_fp8(x) for x in (q, k, v))
@@ -497,7 +498,8 @@ def run_workload(w, steps: int, warmup: int, flush: bool = False, cold: bool = T
                       flops_counted="2.5 x forward (five N x N x d products)")
     if w.splitkv:
         config.update(entry_point="attn_fwd_splitkv",
-                      num_splits=splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim))
+                      num_splits=splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim,
+                                                    w.causal, w.window_left))
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": traffic, "kernel": kernel_name(w, cu),

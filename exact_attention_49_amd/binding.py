@@ -58,9 +58,9 @@ EXPORTED_SYMBOLS = {
                                      _I, _I, _I, _I, _P, _S, _P]),
     "attn_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                                       _I, _I, _P]),
-    "attn_fwd_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "attn_fwd_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
-    "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I]),
+    "attn_fwd_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_varlen_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "attn_fwd_fp8": (_I, [_P] * 8 + [_I] * 6 + [_F] + [_I] * 3 + [_P]),
     "attn_fwd_varlen_fp8": (_I, [_P] * 9 + [_I] * 7 + [_F] + [_I] * 3 + [_P]),
@@ -316,9 +316,11 @@ def attn_fwd_varlen_persistent(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     return out, lse
 
 
-def splitkv_num_splits(batch: int, heads: int, seqlen: int, head_dim: int) -> int:
+def splitkv_num_splits(batch: int, heads: int, seqlen: int, head_dim: int,
+                       causal: bool = False, window_left: int = -1) -> int:
     """The split count the library picks for num_splits = 0 (1 = no split)."""
-    return load_library().attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim)
+    return load_library().attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim,
+                                                      int(bool(causal)), int(window_left))
 
 
 def bwd_workspace_size(batch: int, heads_q: int, seqlen: int) -> int:
@@ -332,10 +334,13 @@ def varlen_bwd_workspace_size(total_tokens: int, heads_q: int) -> int:
 
 
 def splitkv_workspace_size(batch: int, heads: int, seqlen: int, head_dim: int,
-                           num_splits: int = 0) -> int:
-    """Workspace bytes attn_fwd_splitkv needs (0: none)."""
+                           num_splits: int = 0, causal: bool = False,
+                           window_left: int = -1) -> int:
+    """Workspace bytes attn_fwd_splitkv needs (0: none); the mask arguments matter for
+    num_splits = 0 only."""
     return load_library().attn_fwd_splitkv_workspace_size(batch, heads, seqlen, head_dim,
-                                                          num_splits)
+                                                          num_splits, int(bool(causal)),
+                                                          int(window_left))
 
 
 def varlen_splitkv_num_splits(num_seqs: int, max_seqlen: int, total_tokens: int, heads: int,
@@ -361,7 +366,8 @@ def attn_fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
     bsz, nh, hkv, n, d, scale, out, lse = _dense_args(q, k, v, softmax_scale, out, lse,
                                                       return_lse, grouped=True)
     lib = load_library()
-    nbytes = lib.attn_fwd_splitkv_workspace_size(bsz, nh, n, d, int(num_splits))
+    nbytes = lib.attn_fwd_splitkv_workspace_size(bsz, nh, n, d, int(num_splits),
+                                                 int(bool(causal)), int(window_left))
     ws = _workspace(nbytes, workspace, q.device)
     st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr() if lse is not None else None, bsz, nh, hkv, n, d,

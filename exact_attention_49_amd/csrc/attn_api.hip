@@ -1,6 +1,7 @@
 // C ABI of the exact-attention forward library: argument validation, kernel selection and
 // launch.  Declared in include/exact_attn.h.  Validation runs entirely on the host and before
 // any HIP call, so a rejected call touches neither the device nor the stream.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -201,7 +202,7 @@ int launch_split(int head_dim, const xattn::FwdArgs& a, const xattn::MergeArgs& 
                  int mode, long n_work, void* stream) {
   const long grid = n_work * a.num_splits;
   if (n_work <= 0) return ATTN_OK;
-  if (grid > std::numeric_limits<int>::max() || (m.rows + 3) / 4 > 0x7fffffffL)
+  if (grid > std::numeric_limits<int>::max() || (m.rows + 1) / 2 > 0x7fffffffL)  // merge grid
     return ATTN_ERR_TOO_LARGE;
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -369,13 +370,24 @@ Plan plan_varlen(const void* q, const void* k, const void* v, void* o, float* ls
 // Split count for num_splits = 0: enough work items to give every CU its resident share of
 // small-shape workgroups, keeping at least eight K/V tiles per split (shorter splits cost more
 // in merge traffic and per-workgroup set-up than they gain); 1 when the plain grid already
-// fills the chip.  Chosen by measurement on MI355X over dense and causal shapes.
-int auto_splits(long n_work, int max_len, int head_dim) {
+// fills the chip.  `spread`: a dense causal grid of at most SPLIT_SPREAD_HEADS (batch, head)
+// pairs, whose items are dealt out to the XCDs one by one (decode_work) and range from one key
+// tile to all of them; with the heaviest items at twice the mean, one item per slot would leave
+// the chip on a tail of them, and twice the items balance it, as long as a split of the longest
+// range keeps 16 key tiles (its items average half of that).  Chosen by measurement on MI355X
+// over dense and causal shapes (d = 128 causal, 4 splits against 2: B1 H2 N16384 251 -> 194 us,
+// B1 H1 N32768 366 -> 320 us; with more heads, B1 H8 N4096, 2 splits stay best: 77 vs 82 us;
+// B1 H1 N8192, 16 splits against 8: 69 vs 64 us).
+int auto_splits(long n_work, int max_len, int head_dim, bool spread) {
   const long target = (long)device_cus() * resident_per_cu(head_dim);
-  if (n_work <= 0 || n_work >= target) return 1;
   const int tiles = (max_len + small_tile_keys(head_dim) - 1) / small_tile_keys(head_dim);
-  long s = (target + n_work - 1) / n_work;
-  if (s > tiles / 8) s = tiles / 8;
+  auto count = [&](long items, int min_tiles) -> long {
+    if (n_work <= 0 || n_work >= items) return 1;
+    const long s = (items + n_work - 1) / n_work;
+    return s < tiles / min_tiles ? s : tiles / min_tiles;
+  };
+  long s = count(target, 8);
+  if (spread) s = std::max(s, count(2 * target, 16));
   if (s > kMaxSplits) s = kMaxSplits;
   return s < 1 ? 1 : (int)s;
 }
@@ -586,20 +598,30 @@ int attn_fwd_varlen_persistent(const void* q, const void* k, const void* v, void
   return launch_persistent(p.a, dtype, p.mode, p.n_work, stream);
 }
 
-int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim) {
+// Whether a dense split-KV call deals its items out to the XCDs one by one (decode_work): a
+// causal mask without a left window, over at most SPLIT_SPREAD_HEADS (batch, head) pairs.
+bool split_spread(int batch, int heads, int seqlen, int causal, int window_left) {
+  return causal && (window_left < 0 || window_left >= seqlen) &&
+         (long)batch * heads <= xattn::SPLIT_SPREAD_HEADS;
+}
+
+int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim, int causal,
+                                int window_left) {
   if (batch <= 0 || heads <= 0 || seqlen <= 0 || !supported_head_dim(head_dim)) return 1;
   const int br = block_rows(head_dim, false);
   const long n_work = (long)batch * heads * ((seqlen + br - 1) / br);
-  return auto_splits(n_work, seqlen, head_dim);
+  return auto_splits(n_work, seqlen, head_dim,
+                     split_spread(batch, heads, seqlen, causal, window_left));
 }
 
 size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
-                                       int num_splits) {
+                                       int num_splits, int causal, int window_left) {
   if (batch <= 0 || heads <= 0 || seqlen <= 0 || !supported_head_dim(head_dim) ||
       num_splits < 0 || num_splits > kMaxSplits)
     return 0;
-  const int s = num_splits ? num_splits : attn_fwd_splitkv_num_splits(batch, heads, seqlen,
-                                                                      head_dim);
+  const int s = num_splits ? num_splits
+                           : attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim, causal,
+                                                         window_left);
   return workspace_bytes_for((long)batch * heads * seqlen, head_dim, s);
 }
 
@@ -611,7 +633,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   Plan p = plan_dense(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
                       softmax_scale, causal, window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  const int s = num_splits ? num_splits
+                           : attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim, causal,
+                                                         window_left);
   if (s == 1)
     return attn_fwd_gqa(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
                         softmax_scale, causal, window_left, window_right, stream);
@@ -626,7 +650,12 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
   Plan p = plan_dense(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
                       softmax_scale, causal, window_left, window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  int s = num_splits;
+  if (s == 0) {  // the library's choice, lowered to the largest count whose partials fit
+    s = attn_fwd_splitkv_num_splits(batch, heads, seqlen, head_dim, causal, window_left);
+    while (s > 1 && workspace_bytes_for(p.rows, head_dim, s) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+      --s;
+  }
   if (s == 1)  // the plain kernels need no scratch
     return attn_fwd_gqa(q, k, v, o, lse, batch, heads, heads_kv, seqlen, head_dim, dtype,
                         softmax_scale, causal, window_left, window_right, stream);
@@ -647,7 +676,7 @@ int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_t
   const long by_total = ((long)total_tokens + br - 1) / br + num_seqs;
   const long by_max = (long)num_seqs * ((max_seqlen + br - 1) / br);
   return auto_splits((long)heads * (by_total < by_max ? by_total : by_max), max_seqlen,
-                     head_dim);
+                     head_dim, false);
 }
 
 size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int total_tokens,
@@ -672,7 +701,7 @@ int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o
                        heads_kv, head_dim, dtype, softmax_scale, causal, window_left,
                        window_right, 0);
   if (p.status != ATTN_OK || p.empty) return p.status;
-  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim);
+  const int s = num_splits ? num_splits : auto_splits(p.n_work, p.max_len, head_dim, false);
   if (s == 1)
     return attn_fwd_varlen_gqa(q, k, v, o, lse, cu_seqlens, num_seqs, max_seqlen,
                                total_tokens, heads, heads_kv, head_dim, dtype, softmax_scale,

@@ -402,18 +402,30 @@ __device__ __forceinline__ Decoded decode_slot(const FwdArgs& a, int wid, int ns
   return d;
 }
 
-// Map this workgroup of a plain grid (one work slot per workgroup, XCD-remapped) to its slot
-// and, in split-KV mode, a split (the splits of one q-tile are neighbours: they share its Q
-// rows).
+// Map this workgroup of a plain grid (one work slot per workgroup) to its slot and, in
+// split-KV mode, a split (the splits of one q-tile are neighbours: they share its Q rows).
+// The grid is XCD-remapped, so that an XCD runs a contiguous range of the work list: whole
+// heads, whose K/V its L2 then holds, or neighbouring q-tiles, which share most of a window's
+// K/V.  A dense causal split-KV grid over at most SPLIT_SPREAD_HEADS (batch, head) pairs is
+// not: its heads are long and each fills several XCDs, and a contiguous range of a causal
+// head's heaviest-first list would give one XCD all of its heaviest q-tiles (B1 H2 N16384: one
+// XCD with 1.7x the mean work).  Workgroup i then runs item i, on XCD i % 8, so every XCD
+// takes every eighth item of that list.
+// (Measured on MI355X with 2 and 4 splits: B1 H3 N16384 d = 128 331 -> 270 us dealt out one
+// by one; at 4 pairs, B1 H4 N8192, no gain at d = 128 and 97 -> 108 us at d = 64.)
+constexpr int SPLIT_SPREAD_HEADS = 3;
 template <int BR, int MODE, bool SPLIT = false>
 __device__ __forceinline__ Decoded decode_work(const FwdArgs& a, Work& w, int rows = BR) {
-  int wid = xcd_remap(blockIdx.x, gridDim.x);
+  int wid = blockIdx.x;
   w.split = 0;
   int nslots = gridDim.x;
+  if constexpr (SPLIT) nslots /= a.num_splits;
+  if (!(SPLIT && MODE == MASK_CAUSAL && a.cu_seqlens == nullptr &&
+        nslots <= SPLIT_SPREAD_HEADS * a.tiles_per_head))
+    wid = xcd_remap(wid, gridDim.x);
   if constexpr (SPLIT) {
     w.split = wid % a.num_splits;
     wid /= a.num_splits;
-    nslots /= a.num_splits;
   }
   return decode_slot<BR, MODE>(a, wid, nslots, w, rows);
 }
@@ -443,12 +455,13 @@ __device__ __forceinline__ int persist_slot(const Persist& p, int k) {
 }
 
 // Split-KV: restrict the key-tile range [t_lo, t_lo + n) of a q-tile to the share of split
-// `split` (contiguous, as equal as integer division allows; possibly empty).
-__device__ __forceinline__ void split_tiles(int split, int num_splits, int& t_lo, int& n) {
-  const int a0 = (int)((long)n * split / num_splits);
-  const int a1 = (int)((long)n * (split + 1) / num_splits);
-  t_lo += a0;
-  n = a1 - a0;
+// `split` (contiguous, as equal as integer division allows; possibly empty).  32-bit
+// arithmetic suffices (n * num_splits < 2^31 for any sequence the buffer loads can address).
+__device__ __forceinline__ void split_tiles(const FwdArgs& a, int split, int& t_lo, int& n) {
+  const unsigned a0 = (unsigned)n * (unsigned)split / (unsigned)a.num_splits;
+  const unsigned a1 = (unsigned)n * (unsigned)(split + 1) / (unsigned)a.num_splits;
+  t_lo += (int)a0;
+  n = (int)(a1 - a0);
 }
 
 // Effective window bounds of a mask mode (-1 = unbounded).
@@ -825,9 +838,9 @@ __device__ __forceinline__ void store_rows_staged(const FwdArgs& a, long row0, i
 }
 
 // Split-KV epilogue for one 32-row block: the normalised fp32 partial O = O / l and its
-// natural-log LSE go to split `split` of the partial arrays (a row with nothing visible in
-// this split gets O = 0, LSE = -inf).  All lanes must call it; rows past the end of the
-// sequence are not stored.
+// natural-log LSE go to split `split` of the partial arrays.  A row with nothing visible in
+// this split gets LSE = -inf and no O (the merge reads no O behind an LSE of -inf).  All lanes
+// must call it; rows past the end of the sequence are not stored.
 template <int D>
 __device__ __forceinline__ void store_rows_partial(const FwdArgs& a, int split, long row0,
                                                    int qrow, int seqlen, int hh,
@@ -836,8 +849,10 @@ __device__ __forceinline__ void store_rows_partial(const FwdArgs& a, int split, 
   constexpr float LN2 = 0.693147180559945309f;
   const float lt = halves_sum(l_run);
   if (qrow >= seqlen) return;
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const long row = (long)split * a.split_rows + row0 + qrow;
+  if (hh == 0) a.lse_part[row] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
+  if (!(lt > 0.f)) return;
+  const float inv = 1.0f / lt;
   float* dst = a.o_part + row * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -848,7 +863,6 @@ __device__ __forceinline__ void store_rows_partial(const FwdArgs& a, int split, 
                          x[4 * g4 + 3] * inv};
       *(f32x4*)(dst + db * 32 + 8 * g4 + 4 * hh) = val;
     }
-  if (hh == 0) a.lse_part[row] = lt > 0.f ? (m_run + fast_log2(lt)) * LN2 : -INFINITY;
 }
 
 }  // namespace xattn

@@ -95,10 +95,11 @@ hipError_t launch_shape(const FwdArgs& a, bool bf16, int mode, int n_work, hipSt
 }
 
 // Split-KV runs on the small shape of a head dim (the one for grids too small to fill the
-// chip); the merge is one wave per row, four rows per workgroup.
+// chip); the merge runs 1024 / D rows per 256-thread workgroup.
 template <int D>
 hipError_t launch_merge_shape(const MergeArgs& m, bool bf16, hipStream_t s) {
-  const long blocks = (m.rows + 3) / 4;
+  constexpr int RPB = MergeShape<D>::RPB;
+  const long blocks = (m.rows + RPB - 1) / RPB;
   if (bf16) return launch_kernel(attn_merge_kernel<true, D>, (unsigned)blocks, 256, s, m);
   return launch_kernel(attn_merge_kernel<false, D>, (unsigned)blocks, 256, s, m);
 }

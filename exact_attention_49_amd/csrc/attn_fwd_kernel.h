@@ -58,7 +58,7 @@ void attn_fwd_kernel(FwdArgs a) {
   if (wl >= 0) k_lo = max(0, q0 - wl);
   if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
   int t_lo = k_lo / BC, n_tiles = k_hi / BC - t_lo + 1;
-  if constexpr (SPLIT) split_tiles(w.split, a.num_splits, t_lo, n_tiles);
+  if constexpr (SPLIT) split_tiles(a, w.split, t_lo, n_tiles);
   const int t_hi = t_lo + n_tiles - 1;
 
   const bool wave_active = qw0 < seqlen;

@@ -131,7 +131,7 @@ void attn_fwd_wide_kernel(FwdArgs a) {
   if (wr >= 0) k_hi = min(seqlen - 1, q_last + wr);
   int t_lo = k_lo / BC;
   int n = k_hi / BC - t_lo + 1;
-  if constexpr (SPLIT) split_tiles(w.split, a.num_splits, t_lo, n);
+  if constexpr (SPLIT) split_tiles(a, w.split, t_lo, n);
 
   const bool wave_active = qw0 < seqlen;
   const int qw_last = min(qw0 + 32, seqlen) - 1;

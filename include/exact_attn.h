@@ -157,13 +157,14 @@ int attn_fwd_varlen_persistent(const void* q, const void* k, const void* v, void
  * The result is the same function as attn_fwd / attn_fwd_varlen, up to rounding (page
  * "flash_fwd_kernel.h" @c272619: split-KV work items, n_split_idx; the merge is the
  * log-sum-exp identity written out).
- *   num_splits     : 1..64, or 0 to let the library choose.  A count of 1 (chosen or given)
- *                    runs the plain kernels and leaves the workspace untouched (it may then be
- *                    NULL).
+ *   num_splits     : 1..64, or 0 to let the library choose (see
+ *                    attn_fwd_splitkv_num_splits).  A count of 1 (chosen
+ *                    or given) runs the plain kernels and leaves the workspace untouched (it
+ *                    may then be NULL).
  *   workspace      : DEVICE memory owned by the caller, 256-byte aligned, of at least
  *                    workspace_size bytes, and workspace_size must be at least what the
- *                    matching *_workspace_size function returns for the same sizes and
- *                    num_splits; otherwise ATTN_ERR_INVALID_ARG.  Its contents on entry do not
+ *                    matching *_workspace_size function returns for the same arguments;
+ *                    otherwise ATTN_ERR_INVALID_ARG.  Its contents on entry do not
  *                    matter and on exit are unspecified; two calls in flight at once must not
  *                    share a workspace.
  *   heads, heads_kv: query heads and key/value heads, as heads_q and heads_kv of the
@@ -190,11 +191,13 @@ int attn_fwd_varlen_splitkv(const void* q, const void* k, const void* v, void* o
  * the library owns, one per GPU, held until the process ends.  The call itself makes no
  * hipMalloc, hipFree or other allocating call; the caller passes inputs and outputs.
  *   - Arguments, layouts, num_splits and results are those of attn_fwd_splitkv; outputs are
- *     bitwise equal to attn_fwd_splitkv's for the same split count.
- *   - ATTN_ERR_SCRATCH_LIMIT when the partials (num_splits x rows x (head_dim + 1) x 4 bytes,
- *     each part 256-byte aligned; attn_fwd_splitkv_workspace_size gives the figure) exceed
- *     ATTN_NOALLOC_SCRATCH_BYTES.  Nothing is launched then.  With one split (chosen or
- *     given) the plain kernels run and the scratch is not touched.
+ *     bitwise equal to attn_fwd_splitkv's for the same split count.  num_splits = 0 takes
+ *     the count attn_fwd_splitkv would choose, lowered to the largest whose partials fit the
+ *     scratch (down to 1, the plain kernels).
+ *   - ATTN_ERR_SCRATCH_LIMIT when a given num_splits needs partials (num_splits x rows x
+ *     (head_dim + 1) x 4 bytes, each part 256-byte aligned; attn_fwd_splitkv_workspace_size
+ *     gives the figure) beyond ATTN_NOALLOC_SCRATCH_BYTES.  Nothing is launched then.  With
+ *     one split (chosen or given) the plain kernels run and the scratch is not touched.
  *   - The scratch belongs to the GPU that runs `stream` (the current device for the null
  *     stream); its address is looked up on the first call there.  Every call on one GPU uses
  *     the same scratch: two calls in flight on that GPU at once (different streams, or host
@@ -208,15 +211,23 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
                              int window_right, int num_splits, void* stream);
 
 /* Workspace bytes the split-KV calls need for these sizes (heads = query heads) and
- * num_splits (0 = the count the library would choose).  0 when no workspace is needed (one
- * split) or the arguments are invalid.  Host-only: no device is touched. */
+ * num_splits (0 = the count the library would choose; for attn_fwd_splitkv that count also
+ * depends on the call's causal and window_left, which are read for num_splits = 0 only).  0
+ * when no workspace is needed (one split) or the arguments are invalid.  Host-only: no device
+ * is touched. */
 size_t attn_fwd_splitkv_workspace_size(int batch, int heads, int seqlen, int head_dim,
-                                       int num_splits);
+                                       int num_splits, int causal, int window_left);
 size_t attn_fwd_varlen_splitkv_workspace_size(int num_seqs, int max_seqlen, int total_tokens,
                                               int heads, int head_dim, int num_splits);
 
-/* The split count num_splits = 0 selects for these sizes (1 = no split).  Host-only. */
-int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim);
+/* The split count num_splits = 0 selects (1 = no split): enough work items to give every CU
+ * its resident share of workgroups, with at least eight key tiles per split and at most 64
+ * splits.  For attn_fwd_splitkv, a causal call without a left window (window_left < 0 or
+ * >= seqlen) over at most 3 (batch, head) pairs takes twice as many items: its q-tiles range
+ * from one key tile to all of them, and the library deals them out to the XCDs one by one.
+ * Host-only. */
+int attn_fwd_splitkv_num_splits(int batch, int heads, int seqlen, int head_dim, int causal,
+                                int window_left);
 int attn_fwd_varlen_splitkv_num_splits(int num_seqs, int max_seqlen, int total_tokens,
                                        int heads, int head_dim);
 

@@ -158,31 +158,49 @@ def test_splitkv_workspace_size_formula(lib):
     def expect(rows, d, ns):
         up = lambda x: (x + 255) // 256 * 256  # noqa: E731
         return up(ns * rows * d * 4) + up(ns * rows * 4)
-    assert lib.attn_fwd_splitkv_workspace_size(2, 3, 1000, 128, 4) == expect(6000, 128, 4)
-    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 77, 64, 3) == expect(77, 64, 3)
+    for causal, wl in ((0, -1), (1, -1), (1, 100)):  # the mask only matters for ns = 0
+        assert lib.attn_fwd_splitkv_workspace_size(2, 3, 1000, 128, 4, causal, wl) == \
+            expect(6000, 128, 4)
+        assert lib.attn_fwd_splitkv_workspace_size(1, 1, 77, 64, 3, causal, wl) == \
+            expect(77, 64, 3)
     assert lib.attn_fwd_varlen_splitkv_workspace_size(5, 300, 1000, 4, 256, 2) == \
         expect(4000, 256, 2)
-    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 1) == 0      # one split
-    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 96, 2) == 0       # bad head dim
-    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 65) == 0     # too many splits
-    assert lib.attn_fwd_splitkv_workspace_size(0, 1, 4096, 128, 2) == 0      # empty
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 1, 0, -1) == 0    # one split
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 96, 2, 0, -1) == 0     # bad head dim
+    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 4096, 128, 65, 0, -1) == 0   # too many
+    assert lib.attn_fwd_splitkv_workspace_size(0, 1, 4096, 128, 2, 0, -1) == 0    # empty
 
 
 def test_splitkv_automatic_count(lib):
-    # a grid that fills the chip needs no split; a single long head does
-    assert lib.attn_fwd_splitkv_num_splits(2, 32, 8192, 128) == 1
-    s = lib.attn_fwd_splitkv_num_splits(1, 1, 16384, 128)
-    assert 2 <= s <= 64
-    assert lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, 0) == \
-        lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, s)
-    # never fewer than eight key tiles per split
-    assert lib.attn_fwd_splitkv_num_splits(1, 1, 256, 128) == 1
-    assert lib.attn_fwd_splitkv_num_splits(1, 1, 4096, 128) == 8
+    for causal in (0, 1):
+        # a grid that fills the chip needs no split; a single long head does
+        assert lib.attn_fwd_splitkv_num_splits(2, 32, 8192, 128, causal, -1) == 1
+        s = lib.attn_fwd_splitkv_num_splits(1, 1, 16384, 128, causal, -1)
+        assert 2 <= s <= 64
+        assert lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, 0, causal, -1) == \
+            lib.attn_fwd_splitkv_workspace_size(1, 1, 16384, 128, s, causal, -1)
+        # never fewer than eight key tiles per split
+        assert lib.attn_fwd_splitkv_num_splits(1, 1, 256, 128, causal, -1) == 1
+        assert lib.attn_fwd_splitkv_num_splits(1, 1, 4096, 128, causal, -1) == 8
     assert lib.attn_fwd_varlen_splitkv_num_splits(2, 8192, 9000, 1, 64) >= 2
     # enough work items for every CU's resident share: four small-shape workgroups per CU at
     # d = 64 (2 heads x 128 q-tiles -> 4 splits), two at d = 128 (-> 2 splits)
-    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 64) == 4
-    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128) == 2
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 64, 0, -1) == 4
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128, 0, -1) == 2
+    # causal without a left window over at most 3 (batch, head) pairs: twice the items
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 64, 1, -1) == 8
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128, 1, -1) == 4
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128, 1, 16384) == 4   # no window
+    assert lib.attn_fwd_splitkv_num_splits(1, 3, 16384, 128, 1, -1) == 3
+    # ... while a split of the longest range keeps 16 key tiles (128 tiles: 8, not 16)
+    assert lib.attn_fwd_splitkv_num_splits(1, 1, 8192, 128, 1, -1) == 8
+    assert lib.attn_fwd_splitkv_num_splits(1, 1, 8192, 128, 0, -1) == 8
+    # ... but not with a sliding window, more pairs, or packed sequences
+    assert lib.attn_fwd_splitkv_num_splits(1, 2, 16384, 128, 1, 1024) == 2
+    assert lib.attn_fwd_splitkv_num_splits(2, 2, 8192, 128, 1, -1) == 2
+    assert lib.attn_fwd_splitkv_num_splits(1, 8, 4096, 128, 1, -1) == 2
+    assert lib.attn_fwd_splitkv_num_splits(1, 8, 4096, 128, 0, -1) == 2
+    assert lib.attn_fwd_varlen_splitkv_num_splits(1, 16384, 16384, 2, 128) == 2
 
 
 @pytest.mark.parametrize("kw,status", [

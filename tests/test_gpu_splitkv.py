@@ -2,8 +2,8 @@
 
 Split-KV computes the same function as the plain path, so the oracle is the same; the cases
 cover every head dim, the mask modes, explicit split counts (including more splits than key
-tiles, so that some splits are empty), packed batches, the automatic count, and the
-low-occupancy workload at full size on sampled rows."""
+tiles, so that some splits are empty), both orders of a causal grid's items over the XCDs,
+packed batches, the automatic count, and the low-occupancy workload at full size."""
 
 import math
 
@@ -63,6 +63,17 @@ def test_more_splits_than_key_tiles(n):
     assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"n={n}")
 
 
+@pytest.mark.parametrize("b,h", [(1, 1), (1, 3), (2, 2), (4, 3)])
+def test_causal_split_work_orders(b, h):
+    # causal grids of at most 3 (batch, head) pairs deal their items out to the XCDs one by
+    # one, larger ones run contiguous ranges per XCD: both cover every (q-tile, split) once
+    _announce(f"causal split order B{b} H{h}")
+    q, k, v = inputs.make_dense(b, h, 1100, 128, "bf16", seed=650 + 10 * b + h)
+    o, lse = _split_dense(q, k, v, True, -1, -1, 4)
+    o_ref, lse_ref = oracle_dense(q, k, v, 1 / math.sqrt(128), True, -1, -1)
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"B{b} H{h}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 512])
 def test_split_matches_plain_path(d):
     _announce(f"split vs plain d={d}")
@@ -108,7 +119,8 @@ def test_workload_splitkv_bf16_d128_h2_n16384_full():
     of both heads against the oracle."""
     w = inputs.WORKLOADS["splitkv_bf16_d128_h2_n16384"]
     _announce(w.name)
-    assert splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim) > 1
+    assert splitkv_num_splits(w.batch, w.heads, w.seqlen, w.head_dim, w.causal,
+                              w.window_left) > 1
     q, k, v = inputs.make_workload(w)
     o, lse = _split_dense(q, k, v, w.causal, w.window_left, w.window_right, 0)
     check_all_heads_dense(q, k, v, o, lse, w.softmax_scale, w.causal, w.window_left,

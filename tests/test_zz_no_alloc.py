@@ -31,9 +31,10 @@ def test_noalloc_rejects_partials_beyond_the_scratch():
     assert lib.attn_status_string(7).decode().startswith("ATTN_ERR_SCRATCH_LIMIT")
     # the largest split-KV problem that fits: partials just under the limit are accepted by
     # the size check (the workspace-size helper gives the same figure)
-    need = lib.attn_fwd_splitkv_workspace_size(1, 2, 16384, 128, 2)
+    need = lib.attn_fwd_splitkv_workspace_size(1, 2, 16384, 128, 3, 0, -1)
     assert 0 < need <= binding.NOALLOC_SCRATCH_BYTES
-    assert lib.attn_fwd_splitkv_workspace_size(1, 2, 16384, 128, 4) > binding.NOALLOC_SCRATCH_BYTES
+    too_big = lib.attn_fwd_splitkv_workspace_size(1, 2, 16384, 128, 4, 0, -1)
+    assert too_big > binding.NOALLOC_SCRATCH_BYTES
     assert _call(lib, 1, 2, 16384, 128, 4) == 7
     # the usual validation still comes first
     assert _call(lib, 1, 2, 16384, 96, 4) == 2
@@ -44,11 +45,29 @@ DEV = torch.device("cuda:0")
 DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
 # (batch, heads, seqlen, head_dim, dtype, causal, window_left, num_splits): a large call,
-# then a smaller one; the large one uses 32 MiB of the scratch (2 automatic splits)
+# then a smaller one; the large one uses 48 MiB of the scratch (the automatic count, 4 splits,
+# lowered to the 3 whose partials fit)
 CALLS = [
     [(1, 2, 16384, 128, "bf16", True, -1, 0), (1, 1, 3000, 64, "fp16", True, 100, 5)],
     [(1, 1, 4096, 512, "fp16", False, -1, 4), (1, 2, 1000, 256, "bf16", False, -1, 3)],
 ]
+
+
+def _noalloc_count(b, h, n, d, causal, wl, ns):
+    """The split count attn_fwd_splitkv_noalloc runs: the given one, or the automatic one
+    lowered to the largest whose partials fit the scratch."""
+    if ns:
+        return ns
+    s = binding.splitkv_num_splits(b, h, n, d, causal, wl)
+    while s > 1 and binding.splitkv_workspace_size(b, h, n, d, s) > binding.NOALLOC_SCRATCH_BYTES:
+        s -= 1
+    return s
+
+
+def test_noalloc_automatic_count_fits_the_scratch():
+    # the first GPU case's automatic count does not fit and is lowered
+    assert binding.splitkv_num_splits(1, 2, 16384, 128, True, -1) == 4
+    assert _noalloc_count(1, 2, 16384, 128, True, -1, 0) == 3
 
 
 @pytest.mark.gpu
@@ -64,7 +83,7 @@ def test_noalloc_matches_splitkv_with_workspace(pair):
         binding.attn_fwd_splitkv_noalloc(qd, kd, vd, causal=causal, window_left=wl, out=o1,
                                          lse=l1, num_splits=ns)
         o2, l2 = binding.attn_fwd_splitkv(qd, kd, vd, causal=causal, window_left=wl,
-                                          num_splits=ns)
+                                          num_splits=_noalloc_count(b, h, n, d, causal, wl, ns))
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), f"call {i}: differs from workspace"
         check_all_heads_dense(q, k, v, o1, l1, 1 / math.sqrt(d), causal, wl, -1, DTYPES[dt],
