@@ -90,6 +90,7 @@ struct FwdArgs {
 // below 2^8, harmless in fp32 and in the 16-bit P operand, and the result is unchanged: O and
 // l are both taken relative to the same reference m, and LSE = m + log2(l).
 constexpr float RESCALE_SLACK = 8.0f;
+constexpr float RESCALE_LIMIT = 256.0f;  // 2^RESCALE_SLACK: the largest weight exp2(s - m)
 
 // Host: launch a kernel that takes one argument block, and return this launch's own status.
 // hipLaunchKernel reports the launch itself; hipGetLastError after a triple-chevron launch
@@ -699,6 +700,51 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[BC / 32], i32x4 (&pf)[
   return alpha;
 }
 
+// The common case of softmax_tile, without the tile's row max: the exponentials against the
+// running reference m_run, their row sum and P.  Any reference gives the same O and LSE (O and
+// l are both taken relative to it); it only has to keep every weight exp2(s - m) in range.
+// So the exponentials are taken first and the lane sums checked after: a lane's BC / 2
+// weights sum to at most FAST_SUM_LIMIT = (BC / 2) * RESCALE_LIMIT, which bounds each of them
+// by 2^13 at BC = 64, far inside fp16's range (the narrowest P operand).  Returns true with
+// l_run and pf updated when every lane's sum is within the limit, and false when some lane's
+// is not (or is not finite), with s overwritten and l_run, pf untouched; the caller then
+// recomputes S and runs softmax_tile.  A failed sum means some weight exceeded
+// RESCALE_LIMIT, so softmax_tile moves the reference and the next tiles pass again.  While some
+// row of the wave has seen no key (m_run = -inf, its first visible tile) it returns false at
+// once, with s untouched.  The weights, sums and P are those softmax_tile computes whenever it
+// keeps the reference, in the same order.
+template <bool BF16, int BC>
+__device__ __forceinline__ bool softmax_tile_fast(f32x16 (&s)[BC / 32], i32x4 (&pf)[BC / 16],
+                                                  float c2, float m_run, float& l_run) {
+  constexpr float FAST_SUM_LIMIT = (BC / 2) * RESCALE_LIMIT;
+  static_assert(FAST_SUM_LIMIT <= 16384.0f, "weights must stay within fp16's range");
+  if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) return false;  // s untouched
+  constexpr int NP = 4;
+  float ps[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) ps[k] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(s[kb][r], c2, -m_run));
+      s[kb][r] = e;
+      ps[r % NP] += e;
+    }
+  const float rs = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  if (__builtin_amdgcn_ballot_w64(!(rs <= FAST_SUM_LIMIT)) != 0) return false;
+  l_run += rs;
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc) {
+    const int kb = kc >> 1, o8 = (kc & 1) * 8;
+    pf[kc] = (i32x4){(int)Elt<BF16>::pack2(s[kb][o8 + 0], s[kb][o8 + 1]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 4], s[kb][o8 + 5]),
+                     (int)Elt<BF16>::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
+  }
+  return true;
+}
+
 template <int D>
 __device__ __forceinline__ void scale_o(f32x16 (&o)[D / 32], float alpha) {
 #pragma unroll
@@ -714,21 +760,39 @@ __device__ __forceinline__ void scale_o(f32x16 (&o)[D / 32], float alpha) {
 // step i + PF - 1 is read before the MFMA of step i; hook(i) runs at the start of step i.
 // RT: the tile uses the shared swizzle (lane_offsets<D, true>), whose second 8-row read has
 // its own offset.
+// The A operand of P V step i (both transpose reads).
+template <int D, bool RT = false>
+__device__ __forceinline__ i32x4 pv_operand(const char* vt, const LaneOffsets<D>& lo, int i) {
+  constexpr int ROWB = D * 2, DB = D / 32;
+  const char* p = vt + lo.vofs(i % DB, i / DB);
+  const char* p8 = RT ? vt + lo.vofs8(i % DB, i / DB) : p + 8 * ROWB;
+  const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
+  const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p8));
+  return (i32x4){a[0], a[1], b[0], b[1]};
+}
+// The operands of the first PF - 1 steps of mma_pv, read ahead of it (before a softmax that
+// ends in a branch, which would otherwise expose their LDS latency).
+template <int D, int PF = 3, bool RT = false> struct PvHead {
+  i32x4 buf[PF - 1];
+};
+template <int D, int PF = 3, bool RT = false>
+__device__ __forceinline__ PvHead<D, PF, RT> pv_head(const char* vt, const LaneOffsets<D>& lo) {
+  PvHead<D, PF, RT> h;
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) h.buf[i] = pv_operand<D, RT>(vt, lo, i);
+  return h;
+}
+
 template <bool BF16, int D, int BC, int PF = 3, bool RT = false, class Hook = NoHook>
 __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
                                        const i32x4 (&pf)[BC / 16], f32x16 (&o)[D / 32],
-                                       const Hook& hook = Hook()) {
-  constexpr int ROWB = D * 2, DB = D / 32, N = (BC / 16) * DB;
-  auto read = [&](int i) XATTN_INLINE {
-    const char* p = vt + lo.vofs(i % DB, i / DB);
-    const char* p8 = RT ? vt + lo.vofs8(i % DB, i / DB) : p + 8 * ROWB;
-    const i32x2 a = __builtin_bit_cast(i32x2, lds_read_tr(p));
-    const i32x2 b = __builtin_bit_cast(i32x2, lds_read_tr(p8));
-    return (i32x4){a[0], a[1], b[0], b[1]};
-  };
+                                       const Hook& hook = Hook(),
+                                       const PvHead<D, PF, RT>* head = nullptr) {
+  constexpr int DB = D / 32, N = (BC / 16) * DB;
+  auto read = [&](int i) XATTN_INLINE { return pv_operand<D, RT>(vt, lo, i); };
   i32x4 buf[PF];
 #pragma unroll
-  for (int i = 0; i < PF - 1; ++i) buf[i] = read(i);
+  for (int i = 0; i < PF - 1; ++i) buf[i] = head ? head->buf[i] : read(i);
   static_for<N>([&](auto ic) XATTN_INLINE {
     constexpr int i = decltype(ic)::value;
     hook(ic);

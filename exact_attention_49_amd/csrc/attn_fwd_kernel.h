@@ -129,16 +129,31 @@ void attn_fwd_kernel(FwdArgs a) {
     if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;  // nothing visible
     const char* kt = smem + s * 2 * TILEB;
     const char* vt = kt + TILEB;
-    f32x16 sacc[BC / 32];
-    mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
-    if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+    f32x16 sacc[BC / 32];
+    auto scores = [&]() XATTN_INLINE {
+      mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
+      if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+    };
+    scores();
+    // the first V operands, read now so that their latency overlaps the softmax (no room for
+    // them in the d = 64 kernel's 128 registers)
+    constexpr bool HEAD = D >= 128;
+    PvHead<D> vhead;
+    if constexpr (HEAD) vhead = pv_head<D>(vt, lo);
     i32x4 pf[BC / 16];
-    bool moved;
-    const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
-    mma_pv<BF16, D, BC>(vt, lo, pf, oacc);
+    // the weights against the running reference when no row needs it moved (the common
+    // case); otherwise the full online-softmax step: on S as it is while some row has seen no
+    // key yet (softmax_tile_fast then leaves it untouched), else on S recomputed from the K
+    // tile, still in LDS
+    if (!softmax_tile_fast<BF16, BC>(sacc, pf, c2, m_run, l_run)) {
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) scores();
+      bool moved;
+      const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
+    }
+    mma_pv<BF16, D, BC>(vt, lo, pf, oacc, NoHook(), HEAD ? &vhead : nullptr);
   };
 
   // ---- C::DMA: direct global -> LDS loads, STAGES - 1 tiles in flight --------------------

@@ -240,11 +240,20 @@ void attn_fwd_wide_kernel(FwdArgs a) {
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
     i32x4 pf[BC / 16];
-    bool moved;
-    const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // wave-uniform, rare
-      agpr_settle(oacc);
-      scale_o_agpr(oacc, alpha);
+    // the weights against the running reference when no row needs it moved (the common
+    // case); otherwise the full online-softmax step: on S as it is while some row has seen no
+    // key yet, else on S recomputed from the K tile, still in LDS
+    if (!softmax_tile_fast<BF16, BC>(sacc, pf, c2, m_run, l_run)) {
+      if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+        mma_scores<BF16, D, BC, PFW>(kt, lo, qf, sacc);
+        if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
+      }
+      bool moved;
+      const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // wave-uniform, rare
+        agpr_settle(oacc);
+        scale_o_agpr(oacc, alpha);
+      }
     }
     mma_pv_agpr<BF16, D, BC, PFW>(vt, lo, pf, oacc);
   };

@@ -149,6 +149,33 @@ def test_workload_varlen_bf16_d64_w1024_full():
 # Properties that hold at any size
 # ---------------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("growth", [3.0, 12.0])
+@pytest.mark.parametrize("dtype", list(DTYPES))
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("mask", ["none", "causal", "window_50_20"])
+def test_scores_growing_along_keys(d, dtype, mask, growth):
+    """Scores that rise from key tile to key tile (about `growth` log2 units per 64 keys), so
+    that the running reference lags the row max: at 3 the new weights stay below the per-lane
+    limit without a move (they reach 2^3 and more), at 12 every tile moves the reference.  Both
+    must give the oracle's result."""
+    _announce(f"growing scores d={d} {dtype} {mask} growth={growth}")
+    m = MASKS[mask]
+    n = 700
+    gen = torch.Generator("cpu").manual_seed(4242 + d)
+    q = 0.25 * torch.randn(1, 2, n, d, generator=gen)
+    q[..., 0] = 1.0
+    k = 0.25 * torch.randn(1, 2, n, d, generator=gen)
+    # S[i, j] = scale * q_i . k_j grows by `growth` log2 units per 64 keys through column 0
+    scale = 1 / math.sqrt(d)
+    k[..., 0] = torch.arange(n, dtype=torch.float32) * (growth / 64 / scale / math.log2(math.e))
+    v = torch.randn(1, 2, n, d, generator=gen)
+    q, k, v = (x.to(DTYPES[dtype]) for x in (q, k, v))
+    o, lse = gpu_dense(q, k, v, m["causal"], m["wl"], m["wr"])
+    o_ref, lse_ref = oracle_dense(q, k, v, scale, m["causal"], m["wl"], m["wr"])
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, DTYPES[dtype],
+                 f"growing d={d} {dtype} {mask} growth={growth}")
+
+
 @pytest.mark.parametrize("mask", ["causal", "causal_w37", "window_50_20"])
 def test_zero_q_gives_log_count(mask):
     """Q = 0: every visible score is 0, so LSE_i = log(#visible keys of row i) and O_i is the
