@@ -74,6 +74,20 @@ def test_causal_split_work_orders(b, h):
     assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"B{b} H{h}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_empty_splits_ignore_workspace_garbage(d):
+    # splits that see no key write LSE = -inf and no partial O: the merge must not read the O
+    # left in the workspace (here NaN), which would poison the row through 0 * NaN
+    _announce(f"empty splits over a NaN workspace d={d}")
+    q, k, v = inputs.make_dense(1, 2, 200, d, "bf16", seed=660 + d)
+    nbytes = splitkv_workspace_size(1, 2, 200, d, 12)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = _split_dense(q, k, v, True, -1, -1, 12, workspace=ws)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    o_ref, lse_ref = oracle_dense(q, k, v, 1 / math.sqrt(d), True, -1, -1)
+    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 512])
 def test_split_matches_plain_path(d):
     _announce(f"split vs plain d={d}")
