@@ -124,7 +124,8 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // ---- one K/V tile: S^T, mask, online softmax, O^T update --------------------------------
-  auto consume = [&](int t, int s) {
+  // (s: the LDS stage, an int or, for the unrolled two-stage sweep, a compile-time constant)
+  auto consume = [&](int t, auto s) {
     const int k0 = t * BC;
     if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;  // nothing visible
     const char* kt = smem + s * 2 * TILEB;
@@ -209,15 +210,31 @@ void attn_fwd_kernel(FwdArgs a) {
     q_arrived<D>(qf);
     wait_older(LEAD == 2 && n_tiles > 1);
     block_barrier();
-    int s = 0;
-    for (int t = t_lo; t <= t_hi; ++t) {
-      // stage (s + LEAD) % STAGES held tile t - 1, free since the last barrier
-      const int sl = s + LEAD < STAGES ? s + LEAD : s + LEAD - STAGES;
-      if (t + LEAD <= t_hi) dma_tile(t + LEAD, sl);
-      consume(t, s);
-      if (t + 1 <= t_hi) wait_older(LEAD == 2 && t + 2 <= t_hi);
-      block_barrier();
-      s = s + 1 < STAGES ? s + 1 : 0;
+    if constexpr (STAGES == 2) {
+      // unrolled by two, so that each tile's stage, and with it every LDS operand address, is
+      // a compile-time constant (immediate offsets instead of address arithmetic per read)
+      auto step = [&](int t, auto stage) XATTN_INLINE {
+        constexpr int S = decltype(stage)::value;
+        if (t + 1 <= t_hi) dma_tile(t + 1, 1 - S);  // stage 1 - S held tile t - 1
+        consume(t, stage);
+        if (t + 1 <= t_hi) wait_older(false);
+        block_barrier();
+      };
+      for (int t = t_lo; t <= t_hi; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 <= t_hi) step(t + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      int s = 0;
+      for (int t = t_lo; t <= t_hi; ++t) {
+        // stage (s + LEAD) % STAGES held tile t - 1, free since the last barrier
+        const int sl = s + LEAD < STAGES ? s + LEAD : s + LEAD - STAGES;
+        if (t + LEAD <= t_hi) dma_tile(t + LEAD, sl);
+        consume(t, s);
+        if (t + 1 <= t_hi) wait_older(LEAD == 2 && t + 2 <= t_hi);
+        block_barrier();
+        s = s + 1 < STAGES ? s + 1 : 0;
+      }
     }
   } else if constexpr (STAGES == 2) {
     if (n_tiles > 0) gload(t_lo);

@@ -124,11 +124,14 @@ def test_gqa_varlen(d, mask):
 def test_gqa_splitkv(d):
     _announce(f"gqa split-KV d={d}")
     m = MASKS["causal"]
-    q, k, v = inputs.make_dense(1, 8, 900, d, "bf16", seed=1300 + d, heads_kv=2)
-    o, lse = attn_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, num_splits=5)
-    torch.cuda.synchronize()
-    o_ref, lse_ref = _oracle(q, k, v, 1 / math.sqrt(d), m)
-    assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16, f"split d={d}")
+    # 8 query heads (work dealt to the XCDs in contiguous ranges) and 3 (dealt item by item)
+    for hq, hkv in ((8, 2), (3, 1)):
+        q, k, v = inputs.make_dense(1, hq, 900, d, "bf16", seed=1300 + d + hq, heads_kv=hkv)
+        o, lse = attn_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, num_splits=5)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = _oracle(q, k, v, 1 / math.sqrt(d), m)
+        assert_close(to64(o), to64(lse), o_ref, lse_ref, torch.bfloat16,
+                     f"split d={d} Hq{hq} Hkv{hkv}")
     lens = [300, 0, 600]
     q, k, v, cu = inputs.make_varlen(3, 0, 0, 4, d, "bf16", seed=1350 + d, lengths=lens,
                                      heads_kv=1)
