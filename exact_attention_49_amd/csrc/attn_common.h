@@ -570,6 +570,18 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// A sweep over tiles t_lo..t_hi that alternates between two LDS stages, tile t_lo in stage 0:
+// step(t, std::integral_constant<int, S>{}) for each tile, unrolled by two so that the stage,
+// and with it every LDS operand address of the step, is a compile-time constant (immediate
+// offsets instead of address arithmetic per read).
+template <class Step>
+__device__ __forceinline__ void sweep_two_stages(int t_lo, int t_hi, Step&& step) {
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= t_hi) step(t + 1, std::integral_constant<int, 1>{});
+  }
+}
+
 // Keeps the compiler from moving instructions across this point, so that operand reads stay
 // ahead of the MFMAs that consume them.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }

@@ -223,7 +223,7 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
     }
   };
 
-  auto consume = [&](int t, int s) {
+  auto consume = [&](int t, auto s) {  // s: the stage, a compile-time constant
     const int k0 = t * BC;
     if (!wave_active || k0 > kw_hi || k0 + BC - 1 < kw_lo) return;
     const char* kt = smem + s * 2 * TILEB;
@@ -313,13 +313,13 @@ void attn_fwd_fp8_kernel(Fp8Args fa) {
   dma_tile(t_lo, 0);
   wait_vmem();
   block_barrier();
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int s = (t - t_lo) & 1;
-    if (t < t_hi) dma_tile(t + 1, s ^ 1);  // held tile t - 1, free since the last barrier
-    consume(t, s);
+  sweep_two_stages(t_lo, t_hi, [&](int t, auto stage) XATTN_INLINE {
+    constexpr int S = decltype(stage)::value;
+    if (t < t_hi) dma_tile(t + 1, 1 - S);  // held tile t - 1, free since the last barrier
+    consume(t, stage);
     if (t < t_hi) wait_vmem();
     block_barrier();
-  }
+  });
 
   if (!wave_active) return;
   // epilogue: O = O * descale_v / l, LSE = (m - 8 + log2 l) ln 2

@@ -211,19 +211,13 @@ void attn_fwd_kernel(FwdArgs a) {
     wait_older(LEAD == 2 && n_tiles > 1);
     block_barrier();
     if constexpr (STAGES == 2) {
-      // unrolled by two, so that each tile's stage, and with it every LDS operand address, is
-      // a compile-time constant (immediate offsets instead of address arithmetic per read)
-      auto step = [&](int t, auto stage) XATTN_INLINE {
+      sweep_two_stages(t_lo, t_hi, [&](int t, auto stage) XATTN_INLINE {
         constexpr int S = decltype(stage)::value;
         if (t + 1 <= t_hi) dma_tile(t + 1, 1 - S);  // stage 1 - S held tile t - 1
         consume(t, stage);
         if (t + 1 <= t_hi) wait_older(false);
         block_barrier();
-      };
-      for (int t = t_lo; t <= t_hi; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 <= t_hi) step(t + 1, std::integral_constant<int, 1>{});
-      }
+      });
     } else {
       int s = 0;
       for (int t = t_lo; t <= t_hi; ++t) {
