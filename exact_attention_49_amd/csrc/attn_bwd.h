@@ -438,7 +438,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   // key krow sees query i iff krow - wr <= i <= krow + wl: the forward's test with the window
   // bounds exchanged.
   i32x4 ph[NPW];
-  auto consume_dv = [&](int qbase, int s) {
+  auto consume_dv = [&](int qbase, auto s) {  // s: the stage, an int or a constant
     const char* qn = smem + s * STAGEB;
     const char* dn = qn + TILEB;
     const float* ls = (const float*)(dn + TILEB);
@@ -472,7 +472,7 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   };
 
   // dK wave, tile it (stage s, P of the tile in pbuf): dP = dO V^T, dS, dK^T += Q^T dS.
-  auto consume_dk = [&](int s) {
+  auto consume_dk = [&](auto s) {
     const char* qn = smem + s * STAGEB;
     const char* dn = qn + TILEB;
     const float* ls = (const float*)(dn + TILEB);
@@ -514,24 +514,30 @@ void attn_bwd_dkdv_kernel(BwdArgs ba) {
   if (n_it > 1) dma_tile(1, 1);
   wait_older(n_it > 1);
   block_barrier();
-  int s = 0;  // it % 3
-  for (int it = 0; it < n_it; ++it) {
-    const int sp = s == 0 ? 2 : s - 1;  // (it - 1) % 3 = (it + 2) % 3
+  // (unrolled by three, so that the stages, and with them the LDS operand addresses, are
+  // compile-time constants)
+  auto step = [&](int it, auto stage) XATTN_INLINE {
+    constexpr int S = decltype(stage)::value;  // it % 3
+    using SP = std::integral_constant<int, (S + 2) % 3>;  // (it - 1) % 3
     const bool act = tile_active(tile_base(it));
     if (!dk_wave) {
-      if (act) consume_dv(tile_base(it), s);
+      if (act) consume_dv(tile_base(it), stage);
     } else if (it >= 1 && tile_active(tile_base(it - 1))) {
-      consume_dk(sp);
+      consume_dk(SP{});
     }
-    block_barrier();  // the dK waves are done with stage sp and with the P of tile it - 1
-    if (it + 2 < n_it) dma_tile(it + 2, sp);
+    block_barrier();  // the dK waves are done with stage SP and with the P of tile it - 1
+    if (it + 2 < n_it) dma_tile(it + 2, SP::value);
     if (!dk_wave && act)
 #pragma unroll
       for (int c = 0; c < NPW; ++c) pbuf[c * 64] = ph[c];
     if (it + 1 < n_it) wait_older(it + 2 < n_it);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the P words are in LDS
     block_barrier();
-    s = s == 2 ? 0 : s + 1;
+  };
+  for (int it = 0; it < n_it; it += 3) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_it) step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < n_it) step(it + 2, std::integral_constant<int, 2>{});
   }
   if (dk_wave && tile_active(tile_base(n_it - 1))) consume_dk((n_it - 1) % 3);
 
