@@ -815,6 +815,44 @@ __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
   });
 }
 
+// mma_pv of one tile and mma_scores of the next as one interleaved sequence: P V step i, then
+// S step i.  The S^T accumulators form only BC / 32 chains, each MFMA depending on the one
+// before it in its block; between two MFMAs of one chain this puts three others.  Each
+// accumulator receives its MFMAs in the same order as in the two separate calls.
+template <bool BF16, int D, int BC, int PF = 3>
+__device__ __forceinline__ void mma_pv_scores(const char* vt, const i32x4 (&pf)[BC / 16],
+                                              f32x16 (&o)[D / 32], const char* kt,
+                                              const i32x4 (&qf)[D / 16], f32x16 (&s)[BC / 32],
+                                              const LaneOffsets<D>& lo) {
+  constexpr int DB = D / 32, KB = BC / 32, N = (BC / 16) * DB;
+  static_assert(N == (D / 16) * KB, "equal step counts");
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  auto vread = [&](int i) XATTN_INLINE { return pv_operand<D, false>(vt, lo, i); };
+  auto kread = [&](int i) XATTN_INLINE {
+    return *(const i32x4*)(kt + lo.kofs(i / KB, i % KB));
+  };
+  i32x4 vbuf[PF], kbuf[PF];
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) {
+    vbuf[i] = vread(i);
+    kbuf[i] = kread(i);
+  }
+  static_for<N>([&](auto ic) XATTN_INLINE {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + PF - 1 < N) vbuf[(i + PF - 1) % PF] = vread(i + PF - 1);
+    sched_fence();
+    o[i % DB] = Elt<BF16>::mfma(vbuf[i % PF], pf[i / DB], o[i % DB]);
+    sched_fence();
+    if constexpr (i + PF - 1 < N) kbuf[(i + PF - 1) % PF] = kread(i + PF - 1);
+    sched_fence();
+    s[i % KB] = Elt<BF16>::mfma(kbuf[i % PF], qf[i / KB], s[i % KB]);
+    sched_fence();
+  });
+}
+
 // Epilogue for one 32-row block: O = O / l (16-bit, round to nearest even) and
 // LSE = (m + log2 l) ln 2.  All lanes must call it (cross-half sum); rows past the end of the
 // sequence are not stored.

@@ -253,8 +253,17 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       }
       if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
     };
-    auto step_pv = [&](int r, const char* vt) XATTN_INLINE {
-      if (sees(r)) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
+    // an MFMA block: O += V_{rp}^T P_{rp}^T (when pv) and S_{rs} = K_{rs} Q^T (when sc),
+    // interleaved when the wave needs both
+    auto step_mfma = [&](bool pv, int rp, const char* vt, bool sc, int rs,
+                         const char* kt) XATTN_INLINE {
+      const bool dp = pv && sees(rp), ds = sc && sees(rs);
+      if (dp && ds) {
+        mma_pv_scores<BF16, D, BC, PF>(vt, pf, oacc, kt, qf, sacc, lo);
+      } else {
+        if (dp) mma_pv<BF16, D, BC, PF>(vt, lo, pf, oacc);
+        if (ds) mma_scores<BF16, D, BC, PF>(kt, lo, qf, sacc);
+      }
     };
 
     // ---- prologue: K_0 (buffer 1), V_0 and K_1 (buffer 0) ---------------------------------
@@ -282,8 +291,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
         if (j < n) step_softmax(j, false, false, 0, 0);
       } else {
         __builtin_amdgcn_s_setprio(2);  // MFMA block: win issue over the partner's softmax
-        if (j >= 1) step_pv(j - 1, vQ);
-        if (j < n) step_scores(j, kQ);
+        step_mfma(j >= 1, j - 1, vQ, j < n, j, kQ);
         __builtin_amdgcn_s_setprio(0);
       }
       if (j >= 1) wait_vmem();  // group B's loads of U_j (issued at half-phase 2j-1)
@@ -291,10 +299,7 @@ void attn_fwd_pp_kernel(FwdArgs a) {
       // half-phase 2j+1
       if (grp_a) {
         __builtin_amdgcn_s_setprio(2);
-        if (j < n) {
-          step_pv(j, vP);
-          if (j + 1 < n) step_scores(j + 1, kP);
-        }
+        if (j < n) step_mfma(true, j, vP, j + 1 < n, j + 1, kP);
         __builtin_amdgcn_s_setprio(0);
       } else {
         if (j < n) step_softmax(j, j + 1 < n, j + 2 < n, vQa, kQa);
