@@ -215,12 +215,11 @@ void attn_bwd_dq_kernel(BwdArgs ba) {
     const char* vn = kn + TILEB;
     f32x16 sacc[BC / 32], dpacc[BC / 32];
     __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the partner wave's VALU work
-    mma_scores<BF16, D, BC>(kn, lo, qf, sacc);
+    mma_scores_two<BF16, D, BC>(kn, qf, sacc, vn, dof, dpacc, lo);  // S and dP
+    __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (k0 + BC > seqlen) || (wr >= 0 && k0 + BC - 1 > qw0 + wr) ||
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
-    mma_scores<BF16, D, BC>(vn, lo, dof, dpacc);
-    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll

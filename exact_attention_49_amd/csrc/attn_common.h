@@ -815,6 +815,46 @@ __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
   });
 }
 
+// Two independent score products of one tile as one interleaved sequence: step i of
+// s0 = T0 B0^T, then step i of s1 = T1 B1^T (T0, T1 tiles in LDS read like K, B0, B1 operands
+// in registers).  Each product alone has only BC / 32 accumulator chains; interleaved, two
+// MFMAs of one chain have three others between them.  Each accumulator receives its MFMAs in
+// the same order as in two mma_scores calls.
+template <bool BF16, int D, int BC, int PF = 3>
+__device__ __forceinline__ void mma_scores_two(const char* t0, const i32x4 (&b0)[D / 16],
+                                               f32x16 (&s0)[BC / 32], const char* t1,
+                                               const i32x4 (&b1)[D / 16], f32x16 (&s1)[BC / 32],
+                                               const LaneOffsets<D>& lo) {
+  constexpr int KB = BC / 32, N = (D / 16) * KB;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[kb][r] = 0.f;
+      s1[kb][r] = 0.f;
+    }
+  auto read = [&](const char* t, int i) XATTN_INLINE {
+    return *(const i32x4*)(t + lo.kofs(i / KB, i % KB));
+  };
+  i32x4 buf0[PF], buf1[PF];
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) {
+    buf0[i] = read(t0, i);
+    buf1[i] = read(t1, i);
+  }
+  static_for<N>([&](auto ic) XATTN_INLINE {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i + PF - 1 < N) buf0[(i + PF - 1) % PF] = read(t0, i + PF - 1);
+    sched_fence();
+    s0[i % KB] = Elt<BF16>::mfma(buf0[i % PF], b0[i / KB], s0[i % KB]);
+    sched_fence();
+    if constexpr (i + PF - 1 < N) buf1[(i + PF - 1) % PF] = read(t1, i + PF - 1);
+    sched_fence();
+    s1[i % KB] = Elt<BF16>::mfma(buf1[i % PF], b1[i / KB], s1[i % KB]);
+    sched_fence();
+  });
+}
+
 // mma_pv of one tile and mma_scores of the next as one interleaved sequence: P V step i, then
 // S step i.  The S^T accumulators form only BC / 32 chains, each MFMA depending on the one
 // before it in its block; between two MFMAs of one chain this puts three others.  Each
