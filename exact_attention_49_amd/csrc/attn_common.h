@@ -817,9 +817,8 @@ __device__ __forceinline__ void mma_pv(const char* vt, const LaneOffsets<D>& lo,
 
 // Two independent score products of one tile as one interleaved sequence: step i of
 // s0 = T0 B0^T, then step i of s1 = T1 B1^T (T0, T1 tiles in LDS read like K, B0, B1 operands
-// in registers).  Each product alone has only BC / 32 accumulator chains; interleaved, two
-// MFMAs of one chain have three others between them.  Each accumulator receives its MFMAs in
-// the same order as in two mma_scores calls.
+// in registers), so that the two streams' operand reads alternate.  Each accumulator receives
+// its MFMAs in the same order as in two mma_scores calls (bit-identical results).
 template <bool BF16, int D, int BC, int PF = 3>
 __device__ __forceinline__ void mma_scores_two(const char* t0, const i32x4 (&b0)[D / 16],
                                                f32x16 (&s0)[BC / 32], const char* t1,
@@ -856,9 +855,9 @@ __device__ __forceinline__ void mma_scores_two(const char* t0, const i32x4 (&b0)
 }
 
 // mma_pv of one tile and mma_scores of the next as one interleaved sequence: P V step i, then
-// S step i.  The S^T accumulators form only BC / 32 chains, each MFMA depending on the one
-// before it in its block; between two MFMAs of one chain this puts three others.  Each
-// accumulator receives its MFMAs in the same order as in the two separate calls.
+// S step i, so that the transposed V reads and the K reads alternate (and the two operand
+// streams share the prefetch window).  Each accumulator receives its MFMAs in the same order
+// as in the two separate calls (bit-identical results).
 template <bool BF16, int D, int BC, int PF = 3>
 __device__ __forceinline__ void mma_pv_scores(const char* vt, const i32x4 (&pf)[BC / 16],
                                               f32x16 (&o)[D / 32], const char* kt,
