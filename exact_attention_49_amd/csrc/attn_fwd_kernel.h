@@ -134,7 +134,9 @@ void attn_fwd_kernel(FwdArgs a) {
                            (wl >= 0 && k0 < qw0 + 31 - wl);
     f32x16 sacc[BC / 32];
     auto scores = [&]() XATTN_INLINE {
+      __builtin_amdgcn_s_setprio(1);  // MFMA runs win issue over the other waves' VALU work
       mma_scores<BF16, D, BC>(kt, lo, qf, sacc);
+      __builtin_amdgcn_s_setprio(0);
       if (need_mask) mask_scores<BC>(sacc, k0, qrow, seqlen, wl, wr, hh);
     };
     scores();
@@ -154,7 +156,9 @@ void attn_fwd_kernel(FwdArgs a) {
       const float alpha = softmax_tile<BF16, BC>(sacc, pf, c2, m_run, l_run, moved);
       if (__builtin_amdgcn_ballot_w64(moved) != 0) scale_o<D>(oacc, alpha);  // wave-uniform
     }
+    __builtin_amdgcn_s_setprio(1);
     mma_pv<BF16, D, BC>(vt, lo, pf, oacc, NoHook(), HEAD ? &vhead : nullptr);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- C::DMA: direct global -> LDS loads, STAGES - 1 tiles in flight --------------------
