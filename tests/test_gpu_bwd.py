@@ -14,8 +14,8 @@ alone.  Two bars, with the forward's bounds TOL = 2e-2 (bf16) and 5e-3 (fp16):
     rather than to the tensor's largest one.
 
 Cases: both head dims and dtypes, every mask mode at a ragged length, GQA and MQA, packed
-batches with empty and one-token sequences, multi-tile grids, determinism, and one head of the
-benchmark shape at full length."""
+batches with empty and one-token sequences, multi-tile grids, determinism, one head of the
+benchmark shape at full length, and 24 seeded random configurations."""
 
 import math
 
@@ -251,3 +251,28 @@ def test_bwd_masked_grid_with_partial_last_group():
     q, k, v = inputs.make_dense(1, 13, 600, 64, "bf16", seed=3100)
     do = inputs.make_upstream(q.shape, "bf16", seed=3101)
     _check_dense(_gpu_dense(q, k, v, do, m), q, k, v, do, 64, m, torch.bfloat16, "B1 H13 N600")
+
+
+def _draw_bwd(i):
+    rng = np.random.default_rng(30260 + i)
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "fp16"]))
+    hkv = int(rng.integers(1, 4))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    mode = int(rng.integers(0, 4))
+    causal, wl, wr = [(False, -1, -1), (True, -1, -1),
+                      (True, int(rng.integers(0, 300)), -1),
+                      (False, int(rng.integers(0, 200)), int(rng.integers(0, 200)))][mode]
+    return d, dtype, hq, hkv, int(rng.integers(1, 3)), int(rng.integers(1, 600)), \
+        dict(causal=causal, wl=wl, wr=wr)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_bwd_random_configuration(i):
+    # seeded random head dim, dtype, grouped heads, batch, length and mask mode, each gradient
+    # against the oracle at the bars above
+    d, dtype, hq, hkv, b, n, m = _draw_bwd(i)
+    _announce(f"bwd random {i}: d={d} {dtype} B{b} H{hq}/{hkv} N{n} {m}")
+    q, k, v = inputs.make_dense(b, hq, n, d, dtype, seed=3100 + i, heads_kv=hkv)
+    do = inputs.make_upstream(q.shape, dtype, seed=3200 + i)
+    _check_dense(_gpu_dense(q, k, v, do, m), q, k, v, do, d, m, DTYPES[dtype], f"random {i}")

@@ -10,7 +10,8 @@ scaled so that its row sum is at least 256.  Per element that bounds
     |O_gpu - O_ref| <= 2^-4 * (P|V|)_i + 2^-18 * sum_{j visible} |V_j| + 2^-8 |O_ref| + 1e-6,
 where P|V| is the attention of |V| (computed by the oracle) and 2^-8 covers the bf16 output.
 A sharp-softmax case, where O is close to one V row, catches key-order mistakes that the bound
-alone could hide."""
+alone could hide; 24 seeded random configurations (head dim, grouped heads, batch, length, mask
+mode, output dtype) cover combinations the listed cases do not."""
 
 import math
 
@@ -202,3 +203,26 @@ def test_workload_fp8_causal_d128_n8192_full():
     with ThreadPoolExecutor(_oracle_workers()) as ex:
         worst = max(ex.map(one, heads))
     assert worst <= 1.0
+
+
+def _draw_fp8(i):
+    rng = np.random.default_rng(40260 + i)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.integers(1, 4))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    mode = int(rng.integers(0, 4))
+    causal, wl, wr = [(False, -1, -1), (True, -1, -1),
+                      (True, int(rng.integers(0, 300)), -1),
+                      (False, int(rng.integers(0, 200)), int(rng.integers(0, 200)))][mode]
+    out = torch.bfloat16 if bool(rng.integers(0, 2)) else torch.float16
+    return d, hq, hkv, int(rng.integers(1, 3)), int(rng.integers(1, 700)), \
+        dict(causal=causal, wl=wl, wr=wr), out
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_fp8_random_configuration(i):
+    # seeded random head dim, grouped heads, batch, length, mask mode and output dtype, against
+    # the bound above
+    d, hq, hkv, b, n, m, out = _draw_fp8(i)
+    _announce(f"fp8 random {i}: d={d} B{b} H{hq}/{hkv} N{n} {m} {out}")
+    _dense_case(b, hq, hkv, n, m, seed=4100 + i, out_dtype=out, d=d)
